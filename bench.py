@@ -1,0 +1,251 @@
+"""Ring attention forward benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the whole hot path over the workload's synthetic input:
+the striped (or contiguous) shard layout of K and V (ra_stripe_permute), then
+ra_ring_forward: every ring step's blockwise attention, the log-sum-exp merges
+and the final normalisation.  Inputs are generated on the host from a seeded
+counter-based generator and are resident in HBM before timing starts.
+
+Printed: one JSON line.  `value` is attention TFLOP/s counting only unmasked
+(query, key) pairs (4 * head_dim FLOPs per pair per query head), over the timed
+steps.  `roofline` describes the block-attention kernel (achieved FLOP rate from
+HIP events on its own stream vs the bf16 dense MFMA peak); `merge` the
+log-sum-exp merge kernel's algorithmic HBM rate; `cpu_baseline` times the CPU
+fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBPS = 8000.0
+
+WORKLOADS = {
+    # Llama-3-8B-shaped causal GQA, 1M tokens striped over 32 positions:
+    # one position's share (32768 queries against 32 KV blocks of 32768).
+    "llama3-8b-gqa-1m-striped-share": dict(B=1, Hq=32, Hkv=8, S=1 << 20, D=128, N=32, layout="striped",
+                                           causal=True, share=31),
+    # causal striped, 8 heads, 256K tokens over 8 positions: one position's share
+    "causal-256k-striped-share": dict(B=1, Hq=8, Hkv=8, S=262144, D=128, N=8, layout="striped", causal=True,
+                                      share=7),
+    # causal contiguous, 32 heads, 32K tokens over 4 positions: the whole ring
+    "causal-32k-contiguous-ring": dict(B=1, Hq=32, Hkv=32, S=32768, D=128, N=4, layout="contiguous",
+                                       causal=True, share=None),
+    # non-causal, 4 heads, 4K tokens, d 64 over 2 positions: the whole ring
+    "noncausal-4k-ring": dict(B=1, Hq=4, Hkv=4, S=4096, D=64, N=2, layout="contiguous", causal=False,
+                              share=None),
+}
+DEFAULT = "llama3-8b-gqa-1m-striped-share"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per block-kernel launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "block_attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(kernel_src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, k_np, v_np, q_rows_fn, n_rows, seed=2):
+    """Time the oracle on n_rows seeded query rows of the workload."""
+    import oracle
+
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S, N, Hq, Hkv = cfg["S"], cfg["N"], cfg["Hq"], cfg["Hkv"]
+    g = Hq // Hkv
+    heads = rng.integers(0, Hq, n_rows)
+    if cfg["share"] is not None:
+        sb = S // N
+        ts = cfg["share"] + N * rng.integers(0, sb, n_rows) if cfg["layout"] == "striped" else \
+            cfg["share"] * sb + rng.integers(0, sb, n_rows)
+    else:
+        ts = rng.integers(0, S, n_rows)
+    pairs = 0
+    t0 = time.perf_counter()
+    for h in np.unique(heads):
+        ii = np.nonzero(heads == h)[0]
+        t = ts[ii].astype(np.int64)
+        oracle.rows(q_rows_fn(int(h), t), k_np[0, h // g], v_np[0, h // g], q_pos=t, causal=cfg["causal"])
+        pairs += int(np.sum(t + 1)) if cfg["causal"] else len(t) * S
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    threads = min(threads, len(os.sched_getaffinity(0)))
+    flops = 4.0 * cfg["D"] * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} seeded query rows of the same workload, full causal key range each, "
+                      f"fp64 ({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ring positions are virtual positions on a single "
+              "MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ra_inputs
+    import ring_attention_step_amd as ra
+
+    cfg = WORKLOADS[args.workload]
+    B, Hq, Hkv, S, D, N, lay = (cfg[k] for k in ("B", "Hq", "Hkv", "S", "D", "N", "layout"))
+    sb = S // N
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ra.load_library()
+
+    log(f"workload {args.workload}: generating inputs")
+    t0 = time.perf_counter()
+    k_np = ra_inputs.normal((B, Hkv, S, D), ra_inputs.STREAM_K, seed=args.seed, dtype="bf16")
+    v_np = ra_inputs.normal((B, Hkv, S, D), ra_inputs.STREAM_V, seed=args.seed, dtype="bf16")
+    if cfg["share"] is not None:
+        i = cfg["share"]
+        t0q, tstride = (i, N) if lay == "striped" else (i * sb, 1)
+        q_np = ra_inputs.normal((B, Hq, S, D), ra_inputs.STREAM_Q, seed=args.seed, dtype="bf16", t0=t0q,
+                                t_stride=tstride, n_rows=sb)
+
+        def q_rows(h, t):
+            r = (t - i) // N if lay == "striped" else t - i * sb
+            return q_np[0][h, r]
+    else:
+        q_np = ra_inputs.normal((B, Hq, S, D), ra_inputs.STREAM_Q, seed=args.seed, dtype="bf16")
+
+        def q_rows(h, t):
+            return q_np[0][h, t]
+    log(f"inputs generated in {time.perf_counter() - t0:.1f} s; uploading")
+
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_g, v_g = to_dev(k_np), to_dev(v_np)
+    k_sh = torch.empty((N, B, Hkv, sb, D), dtype=torch.bfloat16, device=dev)
+    v_sh = torch.empty_like(k_sh)
+    if cfg["share"] is not None:
+        q_sh = to_dev(q_np)[None]
+        first, n_run = cfg["share"], 1
+        q_g = None
+    else:
+        q_g = to_dev(q_np)
+        q_sh = torch.empty((N, B, Hq, sb, D), dtype=torch.bfloat16, device=dev)
+        first, n_run = 0, N
+    o_sh = torch.empty_like(q_sh)
+    lse = torch.empty(q_sh.shape[:4], dtype=torch.float32, device=dev)
+    o_full = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=dev) if q_g is not None else None
+    desc = ra.ring_desc(q_sh, k_sh, n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"])
+    workspace = torch.empty(ra.ra_ring_workspace_size(desc), dtype=torch.uint8, device=dev)
+
+    def step(stats):
+        ra.ra_stripe_permute(k_g, k_sh, layout=lay, inverse=False, n_pos=N)
+        ra.ra_stripe_permute(v_g, v_sh, layout=lay, inverse=False, n_pos=N)
+        if q_g is not None:
+            ra.ra_stripe_permute(q_g, q_sh, layout=lay, inverse=False, n_pos=N)
+        st = ra.ra_ring_forward(q_sh, k_sh, v_sh, o_sh, lse, n_pos=N, first_pos=first, layout=lay,
+                                causal=cfg["causal"], workspace=workspace, stats=stats)
+        if o_full is not None:
+            ra.ra_stripe_permute(o_sh, o_full, layout=lay, inverse=True, n_pos=N)
+        return st
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    totals = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        st = step(True)
+        for key in totals:
+            totals[key] += st[key]
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed / args.steps * 1e3
+    flops_per_step = totals["flops"] / args.steps
+    value = flops_per_step / (ms_per_step * 1e-3) / 1e12
+    log(f"{ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # block-attention kernel roofline: algorithmic FLOPs per launch / mean launch time
+    per_launch_flops = totals["flops"] / max(1, totals["block_launches"])
+    per_launch_ms = totals["block_ms"] / max(1, totals["block_launches"])
+    achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
+    traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",
+                "launches": totals["block_launches"], "mean_launch_ms": round(per_launch_ms, 4)}
+
+    # merge kernel: algorithmic bytes per step.  Per position with c computed
+    # blocks: c - 2 plain folds (read two partials, write one: 12 D + 24 bytes a
+    # row) and one fold that finalises (read two partials, write the bf16 output
+    # and the log-sum-exp: 8 D + 16 + 2 D + 4 bytes a row); c = 1 finalises only.
+    rows_pos = B * Hq * sb
+    merge_bytes = 0
+    for p in range(n_run):
+        c = sum(1 for j in range(N)
+                if not (cfg["causal"] and ra.ra_unmasked_pairs(
+                    sb, sb, True, ra.ra_ring_pair_offset(lay, N, sb, first + p, j)) == 0))
+        if c == 1:
+            merge_bytes += rows_pos * (4 * D + 8 + 2 * D + 4)
+        else:
+            merge_bytes += (c - 2) * rows_pos * (12 * D + 24) + rows_pos * (8 * D + 16 + 2 * D + 4)
+    n_merge = totals["merge_launches"]
+    merge = None
+    if n_merge:
+        gbps = merge_bytes * args.steps / (totals["merge_ms"] * 1e-3) / 1e9
+        merge = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "launches": n_merge,
+                 "mean_launch_ms": round(totals["merge_ms"] / n_merge, 4),
+                 "bytes_per_step": merge_bytes}
+
+    cpu = None
+    if args.cpu_rows > 0:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_rows)
+
+    line = {
+        "metric": "ring-attention fwd TFLOP/s (causal-adjusted) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
+                   "head_dim": D, "ring_positions": N, "layout": lay, "causal": cfg["causal"],
+                   "positions_run": n_run, "first_position": first,
+                   "unmasked_flops_per_step": flops_per_step},
+        "roofline": roofline, "merge": merge, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

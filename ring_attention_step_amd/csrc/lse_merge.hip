@@ -1,0 +1,120 @@
+// Merge of two blockwise partials with the running softmax, and finalisation.
+//
+// "Ring Attention" (Ultralytics glossary), section "How ring attention works":
+// per-step partial results are combined with the same running softmax flash
+// attention uses and the running numerator is divided by the running
+// denominator at the end.  For partials (m_a, l_a, o_a) and (m_p, l_p, o_p):
+//     m = max(m_a, m_p),  w_x = exp(m_x - m)  (0 when m_x = -inf),
+//     l = w_a l_a + w_p l_p,  o = w_a o_a + w_p o_p,
+// and finalisation gives o / l (0 when l = 0) and lse = m + ln l.
+//
+// HBM-bound streaming kernel.  All lanes that handle one row sit in the same
+// wavefront, and every lane reads the row's (m, l) before any lane of the
+// wavefront writes them back, so the in-place update of (m_acc, l_acc) is
+// race-free.  Head_dim columns move as 16-byte vectors when alignment allows.
+#include <cmath>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+template <int VEC>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a, int tpr) {
+    const int lane = threadIdx.x & 63;
+    const int rows_per_wave = 64 / tpr;
+    const int64_t wave_id = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) >> 6;
+    const int64_t row = wave_id * rows_per_wave + lane / tpr;
+    const int g = lane % tpr;
+    if (row >= a.rows) return;
+
+    const float ma = a.m_acc[row], la = a.l_acc[row];
+    float m = ma, wa = 1.f, wp = 0.f, l = la;
+    const bool fold = a.o_p != nullptr;
+    if (fold) {
+        const float mp = a.m_p[row], lp = a.l_p[row];
+        m = fmaxf(ma, mp);
+        wa = (ma == -INFINITY) ? 0.f : expf(ma - m);
+        wp = (mp == -INFINITY) ? 0.f : expf(mp - m);
+        l = wa * la + wp * lp;
+    }
+    const bool finalize = a.o_out != nullptr || a.lse_out != nullptr;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t base = row * a.D;
+    for (int c = g * VEC; c < a.D; c += tpr * VEC) {
+        float o[VEC];
+        if (VEC == 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(a.o_acc + base + c);
+            o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
+            if (fold) {
+                const f32x4 y = *reinterpret_cast<const f32x4*>(a.o_p + base + c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = wa * o[e] + wp * y[e];
+            }
+        } else {
+            o[0] = a.o_acc[base + c];
+            if (fold) o[0] = wa * o[0] + wp * a.o_p[base + c];
+        }
+        if (finalize) {
+            if (a.o_out != nullptr) {
+                if (a.out_dtype == 1) {
+                    __bf16* out = static_cast<__bf16*>(a.o_out) + base + c;
+                    if (VEC == 4) {
+                        const bf16x2 p0 = __builtin_convertvector((f32x2{o[0] * inv, o[1] * inv}), bf16x2);
+                        const bf16x2 p1 = __builtin_convertvector((f32x2{o[2] * inv, o[3] * inv}), bf16x2);
+                        typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+                        *reinterpret_cast<bf16x4*>(out) = bf16x4{p0[0], p0[1], p1[0], p1[1]};
+                    } else {
+                        const bf16x2 p0 = __builtin_convertvector((f32x2{o[0] * inv, 0.f}), bf16x2);
+                        out[0] = p0[0];
+                    }
+                } else {
+                    float* out = static_cast<float*>(a.o_out) + base + c;
+                    if (VEC == 4)
+                        *reinterpret_cast<f32x4*>(out) = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+                    else
+                        out[0] = o[0] * inv;
+                }
+            }
+        } else if (fold) {
+            if (VEC == 4)
+                *reinterpret_cast<f32x4*>(a.o_acc + base + c) = f32x4{o[0], o[1], o[2], o[3]};
+            else
+                a.o_acc[base + c] = o[0];
+        }
+    }
+    if (g == 0) {
+        if (finalize) {
+            if (a.lse_out != nullptr) a.lse_out[row] = l > 0.f ? m + logf(l) : -INFINITY;
+        } else if (fold) {
+            a.m_acc[row] = m;
+            a.l_acc[row] = l;
+        }
+    }
+}
+
+bool aligned(const void* p, uintptr_t n) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+}  // namespace
+
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
+    if (a.rows == 0) return hipSuccess;
+    const bool vec = (a.D % 4 == 0) && aligned(a.o_acc, 16) && aligned(a.o_p, 16) &&
+                     aligned(a.o_out, a.out_dtype == 1 ? 8 : 16);
+    const int units = vec ? a.D / 4 : a.D;
+    int tpr = 1;
+    while (tpr < units && tpr < 64) tpr <<= 1;
+    const int64_t rows_per_block = 256 / tpr;
+    const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    if (vec)
+        hipLaunchKernelGGL(lse_merge_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, tpr);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, tpr);
+    return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,56 @@
+// Internal launch interface between the host runtime (ra_host.cpp) and the
+// HIP kernels.  Not part of the public ABI (include/ra.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace ra {
+
+// One query block against one key/value block.  All lengths fit in int32
+// (checked by the host); mask_offset is clamped to [-q_len, kv_len] so that it
+// fits as well without changing which keys are visible.
+struct BlockArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    float* o;  // [B, Hq, q_len, D] unnormalised numerator
+    float* m;  // [B, Hq, q_len] running max (natural log units)
+    float* l;  // [B, Hq, q_len] sum of exponentials
+    int32_t B, Hq, Hkv, D;
+    int32_t q_len, kv_len;
+    int64_t qs[3], ks[3], vs[3];  // element strides for (b, h, row)
+    float scale;                  // softmax scale (already resolved)
+    int32_t causal;
+    int32_t mask_offset;  // key c visible to row r iff c <= r + mask_offset
+};
+
+// Vector-ALU kernel: binary32 or bfloat16 inputs, any D in [1, 256], fp32 math.
+hipError_t launch_block_simt(const BlockArgs& a, int dtype, hipStream_t s);
+
+// bf16 MFMA kernel (gfx950): D in {64, 128}; 16-byte aligned rows.
+bool mfma_eligible(const BlockArgs& a, int dtype);
+hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s);
+
+struct MergeArgs {
+    int64_t rows;
+    int32_t D;
+    float* o_acc;
+    float* m_acc;
+    float* l_acc;
+    const float* o_p;  // NULL: no partial to fold in
+    const float* m_p;
+    const float* l_p;
+    void* o_out;  // finalise when o_out or lse_out is non-NULL
+    int32_t out_dtype;
+    float* lse_out;
+};
+hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
+
+// Row moves between [BH, S, row] and [N, BH, S/N, row] under a token map.
+hipError_t launch_stripe_permute(int layout, int inverse, int64_t BH, int64_t S, int32_t N,
+                                 int64_t row_bytes, const void* x, void* y, hipStream_t s);
+
+}  // namespace ra

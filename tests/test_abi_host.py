@@ -1,0 +1,180 @@
+"""The C-ABI library on the host (no GPU): exports, mask/work accounting,
+argument validation.  Nothing here launches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import layout
+from ring_attention_step_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ra.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), f"libra.so does not export {name}"
+    assert set(names) == set(B.EXPORTS)
+    assert lib.ra_abi_version() == 1
+
+
+def test_mask_offset_is_floor_division(lib):
+    rng = np.random.Generator(np.random.PCG64(0))
+    for _ in range(2000):
+        q0, k0 = (int(x) for x in rng.integers(-10**6, 10**6, size=2))
+        s = int(rng.integers(1, 40))
+        assert lib.ra_mask_offset(q0, k0, s) == (q0 - k0) // s
+
+
+def test_unmasked_pairs_matches_enumeration(lib):
+    for q_len in range(0, 9):
+        for kv_len in range(0, 9):
+            for off in range(-11, 12):
+                r = np.arange(q_len)[:, None]
+                c = np.arange(kv_len)[None, :]
+                want = int(np.sum(c <= r + off)) if q_len and kv_len else 0
+                assert lib.ra_unmasked_pairs(q_len, kv_len, 1, off) == want
+                assert lib.ra_unmasked_pairs(q_len, kv_len, 0, off) == q_len * kv_len
+    # large sizes stay exact (int64)
+    assert lib.ra_unmasked_pairs(32768, 32768, 1, 0) == 32768 * 32769 // 2
+    assert lib.ra_unmasked_pairs(32768, 32768, 1, -1) == 32768 * 32767 // 2
+
+
+@pytest.mark.parametrize("lay", ["contiguous", "striped"])
+def test_ring_pair_offset_matches_token_maps(lib, lay):
+    """The per-(position, block) mask offset reproduces the global causal rule."""
+    S = 48
+    for n in (1, 2, 3, 4, 8):
+        sb = S // n
+        for i in range(n):
+            ti = layout.tokens_of(i, S, n, lay)
+            for j in range(n):
+                tj = layout.tokens_of(j, S, n, lay)
+                off = B.ra_ring_pair_offset(lay, n, sb, i, j)
+                r = np.arange(sb)[:, None]
+                c = np.arange(sb)[None, :]
+                assert np.array_equal(c <= r + off, tj[None, :] <= ti[:, None])
+                assert lib.ra_unmasked_pairs(sb, sb, 1, off) == int(np.sum(tj[None, :] <= ti[:, None]))
+
+
+def _ring_flops(n, sb, heads, d, lay, causal, i):
+    total = 0
+    for j in range(n):
+        off = B.ra_ring_pair_offset(lay, n, sb, i, j)
+        total += B.ra_unmasked_pairs(sb, sb, causal, off)
+    return 4 * d * heads * total
+
+
+def test_causal_flop_accounting_of_the_benchmark_shapes():
+    # striped, 8 positions of 32768 tokens, 8 heads, d 128: the last position's share
+    assert _ring_flops(8, 32768, 8, 128, "striped", True, 7) == 4 * 128 * 8 * 8 * 32768 * 32769 // 2
+    # striped 1M tokens over 32 positions, 32 query heads
+    f = _ring_flops(32, 32768, 32, 128, "striped", True, 31)
+    assert f == 4 * 128 * 32 * 32 * 32768 * 32769 // 2
+    assert abs(f - 2.8148e14) / 2.8148e14 < 1e-4
+    # contiguous 32768 tokens over 4 positions: the whole ring is the causal triangle
+    full = sum(_ring_flops(4, 8192, 32, 128, "contiguous", True, i) for i in range(4))
+    assert full == 4 * 128 * 32 * 32768 * 32769 // 2
+
+
+def _block_desc(**kw):
+    d = B.ra_block_desc()
+    d.batch, d.q_heads, d.kv_heads, d.head_dim = 1, 4, 2, 64
+    d.q_len, d.kv_len, d.dtype, d.causal, d.scale, d.flags = 16, 16, B.RA_BF16, 1, 0.0, 0
+    d.q_pos0, d.k_pos0, d.pos_stride = 0, 0, 1
+    d.q_strides[:] = [4 * 16 * 64, 16 * 64, 64]
+    d.k_strides[:] = [2 * 16 * 64, 16 * 64, 64]
+    d.v_strides[:] = [2 * 16 * 64, 16 * 64, 64]
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("q_heads", 3, B.RA_ERR_INVALID), ("kv_heads", 0, B.RA_ERR_INVALID), ("head_dim", 0, B.RA_ERR_INVALID),
+    ("head_dim", 300, B.RA_ERR_UNSUPPORTED), ("dtype", 7, B.RA_ERR_UNSUPPORTED), ("causal", 2, B.RA_ERR_INVALID),
+    ("flags", 0x80, B.RA_ERR_UNSUPPORTED), ("pos_stride", 0, B.RA_ERR_INVALID), ("q_len", -1, B.RA_ERR_INVALID),
+    ("kv_len", 1 << 40, B.RA_ERR_INVALID), ("batch", 0, B.RA_ERR_INVALID), ("scale", float("nan"), B.RA_ERR_INVALID),
+])
+def test_block_validation(lib, field, value, status):
+    d = _block_desc(**{field: value})
+    st = lib.ra_block_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == status
+    assert lib.ra_last_error()
+
+
+def test_block_validation_pointers(lib):
+    d = _block_desc()
+    assert lib.ra_block_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.RA_ERR_INVALID
+    assert lib.ra_block_attn_fwd(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.RA_ERR_INVALID
+    assert lib.ra_block_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == B.RA_ERR_INVALID
+    odd = ctypes.c_void_p(0x10001)
+    assert lib.ra_block_attn_fwd(ctypes.byref(d), odd, FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.RA_ERR_INVALID
+    # an empty query block is a no-op, even with null pointers
+    e = _block_desc(q_len=0)
+    assert lib.ra_block_attn_fwd(ctypes.byref(e), None, None, None, None, None, None, None) == B.RA_OK
+
+
+def test_merge_and_permute_validation(lib):
+    m = lib.ra_lse_merge
+    assert m(-1, 64, FAKE, FAKE, FAKE, None, None, None, None, 0, None, None) == B.RA_ERR_INVALID
+    assert m(8, 0, FAKE, FAKE, FAKE, None, None, None, None, 0, None, None) == B.RA_ERR_INVALID
+    assert m(8, 64, FAKE, FAKE, FAKE, FAKE, None, None, None, 0, None, None) == B.RA_ERR_INVALID
+    assert m(8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 5, None, None) == B.RA_ERR_UNSUPPORTED
+    assert m(8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None) == B.RA_ERR_INVALID  # alias
+    assert m(0, 64, None, None, None, None, None, None, None, 0, None, None) == B.RA_OK
+    p = lib.ra_stripe_permute
+    assert p(2, 0, 1, 1, 1, 64, 8, 4, FAKE, ctypes.c_void_p(0x900000), None) == B.RA_ERR_INVALID  # layout
+    assert p(1, 0, 1, 1, 1, 63, 8, 4, FAKE, ctypes.c_void_p(0x900000), None) == B.RA_ERR_INVALID  # S % N
+    assert p(1, 0, 1, 1, 1, 64, 8, 4, FAKE, ctypes.c_void_p(0x10010), None) == B.RA_ERR_INVALID   # overlap
+    assert p(1, 0, 9, 1, 1, 64, 8, 4, FAKE, ctypes.c_void_p(0x900000), None) == B.RA_ERR_UNSUPPORTED
+
+
+def _ring_desc(**kw):
+    d = B.ra_ring_desc()
+    d.batch, d.q_heads, d.kv_heads, d.head_dim = 1, 32, 8, 128
+    d.n_pos, d.first_pos, d.n_run, d.layout = 32, 31, 1, B.RA_STRIPED
+    d.block_len, d.dtype, d.causal, d.scale = 32768, B.RA_BF16, 1, 0.0
+    d.emulate_copy, d.n_streams = 0, 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_ring_workspace_and_validation(lib):
+    n = ctypes.c_size_t()
+    d = _ring_desc()
+    assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
+    rows = 32 * 32768
+    # one accumulator + one partial: (4 d + 8) bytes per row each
+    assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4)
+    e = _ring_desc(emulate_copy=1)
+    assert lib.ra_ring_workspace_size(ctypes.byref(e), ctypes.byref(n)) == B.RA_OK
+    assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2)
+    for kw in ({"first_pos": 32}, {"n_run": 2}, {"layout": 3}, {"n_pos": 0}, {"block_len": 0},
+               {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}):
+        bad = _ring_desc(**kw)
+        assert lib.ra_ring_workspace_size(ctypes.byref(bad), ctypes.byref(n)) != B.RA_OK
+    order = (ctypes.c_int32 * 32)(*([0] * 32))
+    bad = _ring_desc()
+    bad.visit_order = ctypes.cast(order, ctypes.POINTER(ctypes.c_int32))
+    assert lib.ra_ring_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.RA_ERR_INVALID
+    # too small a workspace is refused before anything runs
+    st = lib.ra_ring_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x100000), 1024, None)
+    assert st == B.RA_ERR_WORKSPACE

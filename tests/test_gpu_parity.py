@@ -1,0 +1,366 @@
+"""GPU parity: every C-ABI entry point against the CPU fp64 oracle.
+
+Element by element on seeded inputs at sizes that span several tiles and a
+ragged tail; at the full benchmark sizes on 4096 seeded sampled query rows
+(stratified to include the first and last row of every block and token 0).
+Tolerances are written in tests/gpu_helpers.py: binary32 1e-5 abs (output and
+log-sum-exp); bfloat16 2e-2 abs on the output, 1e-3 abs on the log-sum-exp.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ra_inputs
+import ring_attention_step_amd as ra
+from oracle import layout as olayout
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ra.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ block kernel
+BLOCK_CASES = [
+    # (dtype, head_dim, flags) -- flags 1 forces the vector-ALU kernel
+    ("f32", 16, 0), ("f32", 64, 0), ("f32", 100, 0), ("f32", 256, 0),
+    ("bf16", 64, 0), ("bf16", 128, 0), ("bf16", 128, 1), ("bf16", 48, 0),
+]
+OFFSETS = [None, 0, -1, 37, -150, 400, -400]
+
+
+def _oracle_partial(q, k, v, causal, off):
+    """Oracle partial of one (b, h) block: rows r at position r + off, keys c at c."""
+    n = q.shape[0]
+    pos = np.arange(n, dtype=np.int64) + (off or 0)
+    return oracle.rows(q, k, v, q_pos=pos, causal=causal)
+
+
+@pytest.mark.parametrize("dtype,D,flags", BLOCK_CASES)
+def test_block_partial_matches_oracle(dtype, D, flags):
+    B, Hq, Hkv, q_len, kv_len = 2, 4, 2, 300, 333
+    gh.say("ra_block_attn_fwd", dtype, D, flags)
+    qn = ra_inputs.normal((B, Hq, q_len, D), 0, seed=3, dtype=dtype)
+    kn = ra_inputs.normal((B, Hkv, kv_len, D), 1, seed=3, dtype=dtype)
+    vn = ra_inputs.normal((B, Hkv, kv_len, D), 2, seed=3, dtype=dtype)
+    # q as a strided view ([B, S, H, D] memory) to exercise the stride arguments
+    q = gh.to_device(np.ascontiguousarray(qn.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+    k, v = gh.to_device(kn, dtype), gh.to_device(vn, dtype)
+    tol = gh.TOL[dtype]
+    for off in OFFSETS:
+        causal = off is not None
+        o = torch.full((B, Hq, q_len, D), float("nan"), device="cuda")
+        m = torch.full((B, Hq, q_len), float("nan"), device="cuda")
+        l = torch.full((B, Hq, q_len), float("nan"), device="cuda")
+        ra.ra_block_attn_fwd(q, k, v, o, m, l, causal=causal, q_pos0=(off or 0), k_pos0=0, flags=flags)
+        torch.cuda.synchronize()
+        o, m, l = gh.to_host_f64(o), gh.to_host_f64(m), gh.to_host_f64(l)
+        for b in range(B):
+            for h in range(Hq):
+                r = _oracle_partial(qn[b, h], kn[b, h // 2], vn[b, h // 2], causal, off)
+                empty = np.isneginf(r["m"])
+                assert np.all(np.isneginf(m[b, h][empty])) and np.all(l[b, h][empty] == 0)
+                assert np.all(o[b, h][empty] == 0)
+                ok = ~empty
+                if not ok.any():
+                    continue
+                assert np.max(np.abs(m[b, h][ok] - r["m"][ok])) <= 1e-4
+                assert np.max(np.abs(l[b, h][ok] / r["l"][ok] - 1)) <= tol["lse"]
+                lse = m[b, h][ok] + np.log(l[b, h][ok])
+                assert np.max(np.abs(lse - r["lse"][ok])) <= tol["lse"]
+                out = o[b, h][ok] / l[b, h][ok][:, None]
+                assert np.max(np.abs(out - r["o"][ok])) <= tol["o"], (off, b, h)
+
+
+def test_block_empty_cases():
+    gh.say("ra_block_attn_fwd empty")
+    q = torch.randn(1, 2, 5, 64, device="cuda").bfloat16()
+    k = torch.randn(1, 2, 0, 64, device="cuda").bfloat16()
+    o = torch.full((1, 2, 5, 64), 7.0, device="cuda")
+    m = torch.zeros(1, 2, 5, device="cuda")
+    l = torch.ones(1, 2, 5, device="cuda")
+    ra.ra_block_attn_fwd(q, k, k, o, m, l)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(m)) and torch.all(l == 0) and torch.all(o == 0)
+    q0 = torch.randn(1, 2, 0, 64, device="cuda").bfloat16()
+    e = torch.empty(1, 2, 0, 64, device="cuda")
+    ra.ra_block_attn_fwd(q0, q0, q0, e, e[..., 0], e[..., 0])  # no-op
+
+
+# ------------------------------------------------------------------ merge kernel
+@pytest.mark.parametrize("dtype,D", [("f32", 16), ("bf16", 128), ("bf16", 64), ("f32", 37)])
+def test_merge_matches_oracle(dtype, D):
+    B, H, q_len, kv_len, split = 1, 3, 200, 333, 150
+    gh.say("ra_lse_merge", dtype, D)
+    qn = ra_inputs.normal((B, H, q_len, D), 0, seed=5, dtype=dtype)
+    kn = ra_inputs.normal((B, H, kv_len, D), 1, seed=5, dtype=dtype)
+    vn = ra_inputs.normal((B, H, kv_len, D), 2, seed=5, dtype=dtype)
+    q, k, v = (gh.to_device(x, dtype) for x in (qn, kn, vn))
+    off = 140  # rows < 10 see no key of the second part
+    parts = []
+    for lo, hi in ((0, split), (split, kv_len)):
+        o = torch.empty(B, H, q_len, D, device="cuda")
+        m = torch.empty(B, H, q_len, device="cuda")
+        l = torch.empty(B, H, q_len, device="cuda")
+        ra.ra_block_attn_fwd(q, k[:, :, lo:hi], v[:, :, lo:hi], o, m, l, causal=True, q_pos0=off, k_pos0=lo)
+        parts.append((o, m, l))
+    (oa, ma, la), (ob, mb, lb) = parts
+    # commutativity and the -inf identity
+    o1, m1, l1 = oa.clone(), ma.clone(), la.clone()
+    ra.ra_lse_merge(o1, m1, l1, ob, mb, lb)
+    o2, m2, l2 = ob.clone(), mb.clone(), lb.clone()
+    ra.ra_lse_merge(o2, m2, l2, oa, ma, la)
+    e_o, e_m, e_l = torch.zeros_like(ob), torch.full_like(mb, float("-inf")), torch.zeros_like(lb)
+    ra.ra_lse_merge(e_o, e_m, e_l, ob, mb, lb)
+    torch.cuda.synchronize()
+    assert torch.equal(e_o, ob) and torch.equal(e_m, mb) and torch.equal(e_l, lb)
+    assert torch.allclose(o1, o2, rtol=1e-6, atol=1e-6) and torch.equal(m1, m2)
+    # finalise
+    out = torch.empty(B, H, q_len, D, device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    lse = torch.empty(B, H, q_len, device="cuda")
+    before = (oa.clone(), ma.clone(), la.clone())
+    ra.ra_lse_merge(oa, ma, la, ob, mb, lb, o_out=out, lse_out=lse)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(before, (oa, ma, la)))  # running state untouched
+    out, lse, m1, l1, o1 = (gh.to_host_f64(x) for x in (out, lse, m1, l1, o1))
+    tol = gh.TOL[dtype]
+    for h in range(H):
+        r = oracle.rows(qn[0, h], kn[0, h], vn[0, h], q_pos=np.arange(q_len) + off, causal=True)
+        assert np.max(np.abs(m1[0, h] - r["m"])) <= 1e-4
+        assert np.max(np.abs(o1[0, h] / l1[0, h][:, None] - r["o"])) <= tol["o"]
+        assert np.max(np.abs(out[0, h] - r["o"])) <= tol["o"]
+        assert np.max(np.abs(lse[0, h] - r["lse"])) <= tol["lse"]
+
+
+# ------------------------------------------------------------------ permute
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 1), ("f32", 16), ("bf16", 3)])
+@pytest.mark.parametrize("lay", ["contiguous", "striped"])
+def test_stripe_permute_bit_exact(dtype, D, lay):
+    gh.say("ra_stripe_permute", dtype, D, lay)
+    for n in (1, 2, 4, 8):
+        B, H, S = 2, 3, 16 * n
+        xn = ra_inputs.normal((B, H, S, D), 0, seed=n, dtype=dtype)
+        x = gh.to_device(xn, dtype)
+        y = torch.empty((n, B, H, S // n, D), dtype=x.dtype, device="cuda")
+        ra.ra_stripe_permute(x, y, layout=lay, inverse=False, n_pos=n)
+        back = torch.empty_like(x)
+        ra.ra_stripe_permute(y, back, layout=lay, inverse=True, n_pos=n)
+        torch.cuda.synchronize()
+        want = olayout.to_shards(xn, n, lay)
+        got = y.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else y.cpu().numpy()
+        assert np.array_equal(got, want)
+        assert torch.equal(back, x)
+
+
+# ------------------------------------------------------------------ ring: configs
+def test_config1_page_example_fp32():
+    """4 positions x 8 tokens, d 16, fp32, non-causal: the pages' worked example."""
+    gh.say("ra_ring_forward config1 fp32")
+    for source in ("page", "seeded"):
+        if source == "page":
+            torch.manual_seed(0)
+            qn, kn, vn = (t.numpy()[None, None] for t in torch.randn(3, 32, 16))
+        else:
+            qn, kn, vn = gh.qkv_global(1, 1, 1, 32, 16, "f32", seed=0)
+        qs, ks, vs = (gh.shards_on_device(x, 4, "contiguous", "f32") for x in (qn, kn, vn))
+        o, lse, _ = gh.run_ring(qs, ks, vs, 4, 0, "contiguous", False)
+        full = torch.empty(1, 1, 32, 16, device="cuda")
+        ra.ra_stripe_permute(o, full, layout="contiguous", inverse=True, n_pos=4)
+        torch.cuda.synchronize()
+        r = oracle.rows(qn[0, 0], kn[0, 0], vn[0, 0])
+        got = gh.to_host_f64(full)[0, 0]
+        assert np.max(np.abs(got - r["o"])) <= 1e-5
+        assert np.max(np.abs(gh.to_host_f64(lse).reshape(32) - r["lse"])) <= 1e-5
+        # the page's own criterion: allclose(atol=1e-5) with the default rtol
+        assert np.allclose(got, r["o"], atol=1e-5)
+
+
+def test_config2_noncausal_bf16_all_rows():
+    B, H, S, D, N = 1, 4, 4096, 64, 2
+    gh.say("ra_ring_forward config2")
+    qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
+    qs, ks, vs = (gh.shards_on_device(x, N, "contiguous", "bf16") for x in (qn, kn, vn))
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", False, stats=True)
+    assert st["block_launches"] == 4 and st["merge_launches"] == 2 and st["blocks_skipped"] == 0
+    assert st["flops"] == 4 * D * H * S * S
+    hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "contiguous", 0, False, "bf16")
+
+
+@pytest.mark.timeout(600)
+def test_config3_causal_contiguous_sampled():
+    B, H, S, D, N = 1, 32, 32768, 128, 4
+    gh.say("ra_ring_forward config3")
+    qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
+    qs, ks, vs = (gh.shards_on_device(x, N, "contiguous", "bf16") for x in (qn, kn, vn))
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", True, stats=True)
+    assert st["blocks_skipped"] == N * (N - 1) // 2
+    assert st["flops"] == 4 * D * H * S * (S + 1) // 2
+    sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
+    gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "contiguous", 0, True, "bf16")
+
+
+@pytest.mark.timeout(900)
+def test_config4_causal_striped_full_ring_and_share():
+    B, H, S, D, N = 1, 8, 262144, 128, 8
+    gh.say("ra_ring_forward config4 full ring")
+    qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
+    qs, ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn))
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "striped", True, stats=True)
+    assert st["blocks_skipped"] == 0 and st["flops"] == 4 * D * H * S * (S + 1) // 2
+    sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
+    gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "striped", 0, True, "bf16")
+    # one position's share (the benchmarked unit) equals that position of the full ring, bitwise
+    gh.say("ra_ring_forward config4 share")
+    o7, lse7, st7 = gh.run_ring(qs[7:8].contiguous(), ks, vs, N, 7, "striped", True, stats=True)
+    assert torch.equal(o7[0], o[7]) and torch.equal(lse7[0], lse[7])
+    assert st7["flops"] == 4 * D * H * N * (S // N) * (S // N + 1) // 2
+
+
+@pytest.mark.timeout(1200)
+def test_config5_gqa_striped_share_sampled():
+    """Llama-3-8B-shaped GQA: 32 q heads, 8 kv heads, d 128, 1M tokens over 32
+    striped positions; one position's share (32768 queries x 32 KV blocks)."""
+    Hq, Hkv, S, D, N, i = 32, 8, 1 << 20, 128, 32, 31
+    gh.say("ra_ring_forward config5 inputs")
+    kn = ra_inputs.normal((1, Hkv, S, D), 1, seed=0, dtype="bf16")
+    vn = ra_inputs.normal((1, Hkv, S, D), 2, seed=0, dtype="bf16")
+    q_share = ra_inputs.normal((1, Hq, S, D), 0, seed=0, dtype="bf16", t0=i, t_stride=N, n_rows=S // N)
+    ks = gh.shards_on_device(kn, N, "striped", "bf16")
+    vs = gh.shards_on_device(vn, N, "striped", "bf16")
+    qs = gh.to_device(q_share, "bf16")[None]
+    gh.say("ra_ring_forward config5 share")
+    o, lse, st = gh.run_ring(qs, ks, vs, N, i, "striped", True, stats=True)
+    assert st["block_launches"] == N and st["merge_launches"] == N - 1
+    assert abs(st["flops"] - 2.8148e14) / 2.8148e14 < 1e-4
+    sb = S // N
+    rng = np.random.Generator(np.random.PCG64(1))
+    rows = np.unique(np.concatenate([[0, sb - 1], rng.integers(0, sb, 4094)]))
+    heads = rng.integers(0, Hq, rows.size)
+    sel_t = i + N * rows
+
+    def qrows(h, t):
+        return q_share[0][h, (t - i) // N]
+
+    gh.compare_rows(o, lse, qrows, kn, vn, heads, sel_t, N, "striped", i, True, "bf16")
+
+
+# ------------------------------------------------------------------ ring: invariants
+def _small_ring_inputs(S=2048, H=4, Hkv=4, D=128, N=8, lay="striped", dtype="bf16", seed=7):
+    qn, kn, vn = gh.qkv_global(1, H, Hkv, S, D, dtype, seed=seed)
+    return (qn, kn, vn), tuple(gh.shards_on_device(x, N, lay, dtype) for x in (qn, kn, vn))
+
+
+def test_visit_order_invariance():
+    gh.say("ra_ring_forward visit orders")
+    N, S, H = 8, 2048, 4
+    (qn, kn, vn), (qs, ks, vs) = _small_ring_inputs(S=S, H=H, N=N)
+    rng = np.random.Generator(np.random.PCG64(11))
+    hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    outs = []
+    for order in (None, list(range(N))[::-1], list(rng.permutation(N))):
+        o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True, visit_order=order)
+        gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "striped", 0, True, "bf16")
+        outs.append((o.float(), lse))
+    for o, lse in outs[1:]:
+        assert torch.max(torch.abs(o - outs[0][0])) <= 2e-2
+        assert torch.max(torch.abs(lse - outs[0][1])) <= 1e-4
+
+
+def test_emulated_copy_ring_and_streams_are_bitwise_identical():
+    gh.say("ra_ring_forward emulate_copy / streams / determinism")
+    N = 8
+    _, (qs, ks, vs) = _small_ring_inputs(N=N)
+    ref, ref_lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    for kw in ({}, {"emulate_copy": True}, {"n_streams": 1}, {"n_streams": 3, "emulate_copy": True},
+               {"visit_order": list(range(N))}):
+        o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True, **kw)
+        assert torch.equal(o, ref) and torch.equal(lse, ref_lse), kw
+    # contiguous causal with skipped blocks through the copy path too
+    (qn, kn, vn), (qc, kc, vc) = _small_ring_inputs(N=4, lay="contiguous")
+    a, al, st = gh.run_ring(qc, kc, vc, 4, 0, "contiguous", True, stats=True)
+    b, bl, stb = gh.run_ring(qc, kc, vc, 4, 0, "contiguous", True, emulate_copy=True, stats=True)
+    assert torch.equal(a, b) and torch.equal(al, bl)
+    assert st["blocks_skipped"] == 6 and stb["copy_launches"] == 4 * 4
+
+
+def test_gqa_equals_repeated_kv_heads():
+    gh.say("ra_ring_forward gqa")
+    N, S, Hq, Hkv = 4, 1024, 8, 2
+    (qn, kn, vn), (qs, ks, vs) = _small_ring_inputs(S=S, H=Hq, Hkv=Hkv, N=N)
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    kr, vr = (x.repeat_interleave(Hq // Hkv, dim=2).contiguous() for x in (ks, vs))
+    o2, lse2, _ = gh.run_ring(qs, kr, vr, N, 0, "striped", True)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    hh, tt = np.meshgrid(np.arange(Hq), np.arange(S), indexing="ij")
+    gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "striped", 0, True, "bf16")
+
+
+def test_striped_and_contiguous_agree_after_unpermuting():
+    gh.say("ra_ring_forward striped vs contiguous")
+    N, S, H, D = 4, 2048, 4, 64
+    qn, kn, vn = gh.qkv_global(1, H, H, S, D, "bf16", seed=13)
+    res = {}
+    for lay in ("striped", "contiguous"):
+        qs, ks, vs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn))
+        o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
+        full = torch.empty(1, H, S, D, device="cuda", dtype=torch.bfloat16)
+        ra.ra_stripe_permute(o, full, layout=lay, inverse=True, n_pos=N)
+        lse_full = torch.empty(1, H, S, 1, device="cuda")
+        ra.ra_stripe_permute(lse[..., None].contiguous(), lse_full, layout=lay, inverse=True, n_pos=N)
+        torch.cuda.synchronize()
+        res[lay] = (gh.to_host_f64(full)[0], gh.to_host_f64(lse_full)[0, ..., 0])
+    assert np.max(np.abs(res["striped"][0] - res["contiguous"][0])) <= 2e-2
+    assert np.max(np.abs(res["striped"][1] - res["contiguous"][1])) <= 1e-3
+    o_ref, lse_ref = oracle.attention(qn, kn, vn, causal=True)
+    assert np.max(np.abs(res["striped"][0] - o_ref[0])) <= 2e-2
+    assert np.max(np.abs(res["striped"][1] - lse_ref[0])) <= 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lay", ["contiguous", "striped"])
+def test_brute_force_causal_grid(dtype, lay):
+    gh.say("ra_ring_forward causal grid", dtype, lay)
+    grid = ([(S, N) for S in (1, 2, 3, 7, 8, 9, 16, 33) for N in (1, 2, 4, 8) if S % N == 0]
+            if dtype == "f32" else [(S, N) for S in (128, 256, 512) for N in (1, 2, 4)])
+    D = 16 if dtype == "f32" else 64
+    for S, N in grid:
+        qn, kn, vn = gh.qkv_global(1, 2, 1, S, D, dtype, seed=S * 10 + N)
+        qs, ks, vs = (gh.shards_on_device(x, N, lay, dtype) for x in (qn, kn, vn))
+        o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
+        hh, tt = np.meshgrid(np.arange(2), np.arange(S), indexing="ij")
+        gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, True, dtype)
+
+
+@pytest.mark.timeout(600)
+def test_dominant_self_key_at_scale():
+    """k = 8 q: each row's own key dominates, so O_t = v_t to bf16 rounding; with the
+    keys shifted by one token the dominant key lies in the future and must stay masked."""
+    H, S, D, N = 2, 65536, 128, 8
+    gh.say("ra_ring_forward dominant self key")
+    qn, kn, vn = gh.qkv_global(1, H, H, S, D, "bf16", seed=17, k_from_q_scale=8.0)
+    qs, ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    full = torch.empty(1, H, S, D, device="cuda", dtype=torch.bfloat16)
+    ra.ra_stripe_permute(o, full, layout="striped", inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    v_f = ra_inputs.bf16_to_f32(vn)[0]
+    assert np.max(np.abs(gh.to_host_f64(full)[0] - v_f)) <= 2e-2
+    ksh = ra_inputs.normal((1, H, S, D), 0, seed=17, dtype="bf16", t0=-1, scale=8.0)
+    ks2 = gh.shards_on_device(ksh, N, "striped", "bf16")
+    o2, _, _ = gh.run_ring(qs, ks2, vs, N, 0, "striped", True)
+    full2 = torch.empty_like(full)
+    ra.ra_stripe_permute(o2, full2, layout="striped", inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    dev = np.max(np.abs(gh.to_host_f64(full2)[0][:, 1:-1] - v_f[:, 2:]), axis=-1)
+    assert np.min(dev) > 0.1  # no row collapsed onto its (masked) future key
