@@ -69,34 +69,36 @@ def traffic_from_profile(kernel_src):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, k_np, v_np, q_rows_fn, n_rows, seed=2):
-    """Time the oracle on n_rows seeded query rows of the workload."""
+def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2):
+    """Time the oracle on seeded query rows of the workload, in chunks of 32 rows,
+    until about budget_s seconds of CPU work have been done."""
     import oracle
 
     rng = np.random.Generator(np.random.PCG64(seed))
     S, N, Hq, Hkv = cfg["S"], cfg["N"], cfg["Hq"], cfg["Hkv"]
     g = Hq // Hkv
-    heads = rng.integers(0, Hq, n_rows)
-    if cfg["share"] is not None:
-        sb = S // N
-        ts = cfg["share"] + N * rng.integers(0, sb, n_rows) if cfg["layout"] == "striped" else \
-            cfg["share"] * sb + rng.integers(0, sb, n_rows)
-    else:
-        ts = rng.integers(0, S, n_rows)
-    pairs = 0
-    t0 = time.perf_counter()
-    for h in np.unique(heads):
-        ii = np.nonzero(heads == h)[0]
-        t = ts[ii].astype(np.int64)
-        oracle.rows(q_rows_fn(int(h), t), k_np[0, h // g], v_np[0, h // g], q_pos=t, causal=cfg["causal"])
+    pairs, rows, dt = 0, 0, 0.0
+    while dt < budget_s and rows < max_rows:
+        h = int(rng.integers(0, Hq))
+        if cfg["share"] is not None:
+            sb = S // N
+            r = rng.integers(0, sb, 32)
+            t = cfg["share"] + N * r if cfg["layout"] == "striped" else cfg["share"] * sb + r
+        else:
+            t = rng.integers(0, S, 32)
+        t = np.sort(t).astype(np.int64)
+        qr = q_rows_fn(h, t)
+        t0 = time.perf_counter()
+        oracle.rows(qr, k_np[0, h // g], v_np[0, h // g], q_pos=t, causal=cfg["causal"])
+        dt += time.perf_counter() - t0
         pairs += int(np.sum(t + 1)) if cfg["causal"] else len(t) * S
-    dt = time.perf_counter() - t0
+        rows += len(t)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     threads = min(threads, len(os.sched_getaffinity(0)))
     flops = 4.0 * cfg["D"] * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_rows} seeded query rows of the same workload, full causal key range each, "
-                      f"fp64 ({flops / 1e9:.1f} GFLOP in {dt:.1f} s)"}
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} seeded query rows of this workload (one head per 32-row chunk), each over its "
+                      f"full causal key range, fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
 def main():
@@ -105,7 +107,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-rows", type=int, default=384, help="oracle rows timed for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -228,9 +231,9 @@ def main():
                  "bytes_per_step": merge_bytes}
 
     cpu = None
-    if args.cpu_rows > 0:
-        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
-        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_rows)
+    if args.cpu_seconds > 0:
+        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds)
 
     line = {
         "metric": "ring-attention fwd TFLOP/s (causal-adjusted) + % of MI355X bf16 MFMA peak",

@@ -1,0 +1,96 @@
+"""GPU parity at the full benchmark sizes (run after the small cases).
+
+Causal striped 256K tokens (8 heads, 8 positions), the Llama-3-8B-shaped GQA
+share (1M tokens, 32 positions), and the dominant-self-key construction at 64K
+tokens.  Large configs are checked on 4096 seeded, sampled query rows against
+the CPU fp64 oracle; tolerances as in tests/gpu_helpers.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import ra_inputs
+import ring_attention_step_amd as ra
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ra.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.timeout(900)
+def test_config4_causal_striped_full_ring_and_share():
+    B, H, S, D, N = 1, 8, 262144, 128, 8
+    gh.say("ra_ring_forward config4 full ring")
+    qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
+    qs, ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn))
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "striped", True, stats=True)
+    assert st["blocks_skipped"] == 0 and st["flops"] == 4 * D * H * S * (S + 1) // 2
+    sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
+    gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "striped", 0, True, "bf16")
+    # one position's share (the benchmarked unit) equals that position of the full ring, bitwise
+    gh.say("ra_ring_forward config4 share")
+    o7, lse7, st7 = gh.run_ring(qs[7:8].contiguous(), ks, vs, N, 7, "striped", True, stats=True)
+    assert torch.equal(o7[0], o[7]) and torch.equal(lse7[0], lse[7])
+    assert st7["flops"] == 4 * D * H * N * (S // N) * (S // N + 1) // 2
+
+
+@pytest.mark.timeout(1200)
+def test_config5_gqa_striped_share_sampled():
+    """Llama-3-8B-shaped GQA: 32 q heads, 8 kv heads, d 128, 1M tokens over 32
+    striped positions; one position's share (32768 queries x 32 KV blocks)."""
+    Hq, Hkv, S, D, N, i = 32, 8, 1 << 20, 128, 32, 31
+    gh.say("ra_ring_forward config5 inputs")
+    kn = ra_inputs.normal((1, Hkv, S, D), 1, seed=0, dtype="bf16")
+    vn = ra_inputs.normal((1, Hkv, S, D), 2, seed=0, dtype="bf16")
+    q_share = ra_inputs.normal((1, Hq, S, D), 0, seed=0, dtype="bf16", t0=i, t_stride=N, n_rows=S // N)
+    ks = gh.shards_on_device(kn, N, "striped", "bf16")
+    vs = gh.shards_on_device(vn, N, "striped", "bf16")
+    qs = gh.to_device(q_share, "bf16")[None]
+    gh.say("ra_ring_forward config5 share")
+    o, lse, st = gh.run_ring(qs, ks, vs, N, i, "striped", True, stats=True)
+    assert st["block_launches"] == N and st["merge_launches"] == N - 1
+    assert abs(st["flops"] - 2.8148e14) / 2.8148e14 < 1e-4
+    sb = S // N
+    rng = np.random.Generator(np.random.PCG64(1))
+    rows = np.unique(np.concatenate([[0, sb - 1], rng.integers(0, sb, 4094)]))
+    heads = rng.integers(0, Hq, rows.size)
+    sel_t = i + N * rows
+
+    def qrows(h, t):
+        return q_share[0][h, (t - i) // N]
+
+    gh.compare_rows(o, lse, qrows, kn, vn, heads, sel_t, N, "striped", i, True, "bf16")
+
+
+@pytest.mark.timeout(600)
+def test_dominant_self_key_at_scale():
+    """k = 8 q: each row's own key dominates, so O_t = v_t to bf16 rounding; with the
+    keys shifted by one token the dominant key lies in the future and must stay masked."""
+    H, S, D, N = 2, 65536, 128, 8
+    gh.say("ra_ring_forward dominant self key")
+    qn, kn, vn = gh.qkv_global(1, H, H, S, D, "bf16", seed=17, k_from_q_scale=8.0)
+    qs, ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    full = torch.empty(1, H, S, D, device="cuda", dtype=torch.bfloat16)
+    ra.ra_stripe_permute(o, full, layout="striped", inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    v_f = ra_inputs.bf16_to_f32(vn)[0]
+    assert np.max(np.abs(gh.to_host_f64(full)[0] - v_f)) <= 2e-2
+    ksh = ra_inputs.normal((1, H, S, D), 0, seed=17, dtype="bf16", t0=-1, scale=8.0)
+    ks2 = gh.shards_on_device(ksh, N, "striped", "bf16")
+    o2, _, _ = gh.run_ring(qs, ks2, vs, N, 0, "striped", True)
+    full2 = torch.empty_like(full)
+    ra.ra_stripe_permute(o2, full2, layout="striped", inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    dev = np.max(np.abs(gh.to_host_f64(full2)[0][:, 1:-1] - v_f[:, 2:]), axis=-1)
+    assert np.min(dev) > 0.1  # no row collapsed onto its (masked) future key
