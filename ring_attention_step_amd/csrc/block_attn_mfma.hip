@@ -8,31 +8,48 @@
 // Orientation.  Both products are computed transposed so that softmax state
 // stays lane-local and P never leaves registers:
 //     S^T[key, q] = K . Q^T     (A = K tile from LDS, B = Q held in registers)
-//     O^T[d, q]  += V^T . P^T   (A = V^T tile from LDS, B = P from the S^T
-//                                accumulators, converted to bf16)
+//     O^T[d, q]  += V^T . P^T   (A = V^T read transposed from LDS, B = P from
+//                                the S^T accumulators, converted to bf16)
 // with v_mfma_f32_32x32x16_bf16.  For that instruction lane l supplies row
 // (l % 32) of A and column (l % 32) of B, each as 8 consecutive k-elements
 // starting at 8 * (l / 32); accumulator register v of lane l holds row
-// 8*(v/4) + 4*(l/32) + v%4, column l % 32.  So lane l owns query l % 32: its
-// 16 S^T registers of a 32-key sub-tile are 16 of that query's keys, and its
-// O^T registers are head_dim columns of that query's output row.  The other
+// 8*(v/4) + 4*(l/32) + v%4, column l % 32.  So lane l owns query l % 32: its 16
+// S^T registers of a 32-key sub-tile are 16 of that query's keys, and its O^T
+// registers are head_dim columns of that query's output row.  The other
 // half-wave (l ^ 32) holds the remaining keys / columns of the same query,
 // reached with v_permlane32_swap for the row max and the final row sum.
 //
-// Feeding P^T as the B operand of the PV product needs each lane's 8 k-values
-// (keys) to match the 8 accumulator registers it already has: registers
-// 8kk..8kk+7 of sub-tile `sub` hold keys 32sub + 16kk + 8(e/4) + 4h + e%4.
-// V^T is therefore staged with its key columns permuted by swapping bits 2
-// and 3 of the in-tile key index (slot = swap23(key)), which makes every A
-// operand read of V^T one contiguous 16-byte LDS load.
+// P^T as the B operand: accumulator registers 8kk..8kk+7 of sub-tile `sub`
+// hold keys 32sub + 16kk + 8(e/4) + 4h + e%4 (h = l / 32, e = 0..7), i.e. two
+// runs of four consecutive keys.  ds_read_b64_tr_b16 returns to each lane of a
+// 16-lane group four consecutive rows of one column of a row-major tile (lane
+// i of the group gets element i%4 of the 8-byte chunk addressed by group lane
+// 4k + i/4, for k = 0..3), so two such reads of the row-major V tile give each
+// lane exactly its 8 V^T elements in the same key order.  V therefore stays
+// in its natural layout and moves HBM -> LDS untouched.
 //
-// Work decomposition: a workgroup of 4 waves owns 128 query rows of one
-// (b, q-head); each wave owns 32 rows.  Keys are visited in tiles of 64.
-// Causal masking uses the block's mask offset: tiles past the last visible key
-// are never loaded, waves with no visible key in a tile skip it, and the
-// element mask is applied only on tiles that straddle the diagonal (or the
-// ragged end of the block).  Tiles are dispatched heaviest first and grouped so
-// that workgroups of one head land on the same XCD (shared L2 for K/V).
+// Data movement.  K and V tiles (64 keys x head_dim) are copied HBM -> LDS by
+// global_load_lds_dwordx4 (no register staging), double buffered: the copy of
+// tile t+1 is issued before tile t is computed, one barrier per tile.  16-byte
+// chunk c of tile row r is stored at chunk position c ^ swz(r); swz permutes
+// the chunk positions of 8 consecutive rows so that the K operand reads (8
+// rows, one chunk) and the V^T transposed reads (4 rows, two adjacent chunks)
+// hit distinct LDS banks.
+//
+// Online softmax.  The running maximum used as the exponent's reference is
+// only moved when a row's maximum grows by more than kTau (log2 units), so the
+// O rescale (one multiply per accumulator register) is rare; probabilities are
+// then bounded by 2^kTau, harmless in fp32 and bf16.  The true row maximum is
+// tracked separately and the partial is re-referenced to it once at the end,
+// so the emitted (m, l, o) are exactly the block's partial.
+//
+// Work decomposition: a workgroup of WAVES waves owns 32*WAVES query rows of
+// one (b, q-head); each wave owns 32 rows.  Causal masking uses the block's
+// mask offset: tiles past the last visible key are never loaded, waves with no
+// visible key in a tile skip it, and the element mask is applied only on
+// tiles that straddle the diagonal (or the ragged end of the block).  Tiles
+// are dispatched heaviest first and grouped so that one head's workgroups land
+// on the same XCD (shared L2 for K/V).
 #include <cmath>
 
 #include "ra_internal.h"
@@ -45,17 +62,18 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
 
-constexpr int kMq = 128;       // query rows per workgroup
-constexpr int kNk = 64;        // keys per tile
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kNk = 64;  // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
-// Swap bits 2 and 3 of an in-tile key index (an involution).
-__device__ inline int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)((char*)(p)))
+
+// Chunk-position permutation of the 8 rows r, r+1, ... (r % 8 == 0).
+__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
 // Combine a lane's value with lane ^ 32's (v_permlane32_swap exchanges halves).
 __device__ inline float xhalf_max(float x) {
@@ -89,16 +107,37 @@ __device__ inline bf16x8 pack_bf16x8(const f32x16& x, int base) {
     return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a) {
-    constexpr int KSTR = D + 8;    // K tile row stride in LDS (bf16), 16-byte pad
-    constexpr int VSTR = kNk + 8;  // V^T tile row stride in LDS (bf16), 16-byte pad
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kNk * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at "no wait").
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane HBM -> LDS (global_load_lds_dwordx4): lane l's bytes land at
+// LDS byte address lds_base + 16 l.  Issued from inline assembly so that the
+// compiler's wait-count pass does not treat the prefetch of the next tile as a
+// hazard for reads of the current one; completion is awaited explicitly
+// (wait_vmem_all) before the barrier that publishes a tile.
+__device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds_base)
+        : "memory", "m0");
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs a) {
+    constexpr int kMq = 32 * WAVES;
+    constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
+    constexpr int TILE_BYTES = kNk * D * 2;    // one K (or V) tile
+    constexpr int INSTR = TILE_BYTES / 1024;   // 1 KiB copy instructions per tile
+    constexpr int PER_WAVE = INSTR / WAVES;
+    static_assert(INSTR % WAVES == 0, "tile copy must split evenly over waves");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE_BYTES];  // [stage][K, V]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qi = lane & 31;
     const int half = lane >> 5;
 
@@ -144,51 +183,58 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
         }
     }
 
+    // Copy of tile t into stage s: instruction i of this wave fills LDS chunk
+    // positions [64 i', 64 i' + 64) of the K and V tiles (i' = wave-major index);
+    // each lane fetches the global chunk that belongs at its position.  Rows past
+    // the block re-read its last row (finite values; they are masked).
+    const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
+    auto issue_tile = [&](int t, int s) {
+        const uint32_t kdst = lds0 + s * 2 * TILE_BYTES;
+        const uint32_t vdst = kdst + TILE_BYTES;
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int inst = wave * PER_WAVE + i;
+            const int pos = inst * 64 + lane;
+            const int r = pos / CPR;
+            const int c = (pos % CPR) ^ swz(r);
+            const int key = min(t * kNk + r, a.kv_len - 1);
+            lds_dma16(kp + key * ks2 + c * 8, kdst + inst * 1024);
+            lds_dma16(vp + key * vs2 + c * 8, vdst + inst * 1024);
+        }
+    };
+
+    // per-lane LDS byte offsets of the operand reads
+    const int sq = swz(qi);  // K rows sub*32 + qi share swz(qi)
+    int koff[D / 16];
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) koff[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
+    const int j = lane & 15;                        // lane within its 16-lane group
+    const int dsub = (lane >> 4) & 1;               // which 16 columns of a 32-column block
+    const int vrow = 4 * half + (j >> 2);           // row within an 8-row run
+    const int sv = swz(vrow);
+    int voff[D / 32];
+#pragma unroll
+    for (int dblk = 0; dblk < D / 32; ++dblk)
+        voff[dblk] = (vrow * CPR + ((4 * dblk + 2 * dsub + ((j & 3) >> 1)) ^ sv)) * 16 + (j & 1) * 8;
+
     const float c2 = a.scale * kLog2e;  // exp(s*scale) = exp2(s*c2)
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY;  // running max, log2 units of the scaled score
-    float l_run = 0.f;        // this lane's share of the running sum
+    float m_ref = -INFINITY;   // exponent reference (log2 units of the scaled score)
+    float m_true = -INFINITY;  // running row maximum
+    float l_run = 0.f;         // this lane's share of the running sum
 
+    if (n_tiles > 0) issue_tile(0, 0);
     for (int t = 0; t < n_tiles; ++t) {
         const int kbase = t * kNk;
+        wait_vmem_all();
         __syncthreads();
-        // K tile -> LDS, row-major: coalesced 16-byte loads and stores.
-        for (int c = tid; c < kNk * D / 8; c += kThreads) {
-            const int kr = c / (D / 8), kc = c % (D / 8);
-            const int key = kbase + kr;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (key < a.kv_len)
-                val = *reinterpret_cast<const u32x4*>(kp + static_cast<int64_t>(key) * a.ks[2] + kc * 8);
-            *reinterpret_cast<u32x4*>(Ks + kr * KSTR + kc * 8) = val;
-        }
-        // V tile -> LDS transposed, key columns in swap23 order.  Each item is
-        // 4 keys x 8 head_dim elements: 4 coalesced 16-byte loads, a register
-        // transpose, 8 8-byte stores.
-        for (int it = tid; it < (D / 8) * (kNk / 4); it += kThreads) {
-            const int dg = it / (kNk / 4), kg = it % (kNk / 4);
-            u32x4 r4[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = kbase + 4 * kg + rr;
-                r4[rr] = u32x4{0u, 0u, 0u, 0u};
-                if (key < a.kv_len)
-                    r4[rr] = *reinterpret_cast<const u32x4*>(vp + static_cast<int64_t>(key) * a.vs[2] + dg * 8);
-            }
-            const int slot = swap23(4 * kg);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const u32x2 lo = {(r4[0][x] & 0xFFFFu) | (r4[1][x] << 16),
-                                  (r4[2][x] & 0xFFFFu) | (r4[3][x] << 16)};
-                const u32x2 hi = {(r4[0][x] >> 16) | (r4[1][x] & 0xFFFF0000u),
-                                  (r4[2][x] >> 16) | (r4[3][x] & 0xFFFF0000u)};
-                *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * x) * VSTR + slot) = lo;
-                *reinterpret_cast<u32x2*>(Vt + (8 * dg + 2 * x + 1) * VSTR + slot) = hi;
-            }
-        }
-        __syncthreads();
+        if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
         if (kbase >= wave_key_end) continue;  // nothing visible to this wave here
+        const char* kst = smem + (t & 1) * 2 * TILE_BYTES;
+        const char* vst = kst + TILE_BYTES;
 
         // S^T = K Q^T for two 32-key sub-tiles.
         f32x16 sacc[2];
@@ -197,8 +243,7 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
             sacc[sub] = f32x16{};
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) {
-                const bf16x8 kop =
-                    *reinterpret_cast<const bf16x8*>(Ks + (sub * 32 + qi) * KSTR + kb * 16 + half * 8);
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kst + sub * 32 * CPR * 16 + koff[kb]);
                 sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kb], sacc[sub], 0, 0, 0);
             }
         }
@@ -221,9 +266,17 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
             }
         }
         mx = xhalf_max(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_true = fmaxf(m_true, mx);
+        const bool move = mx > m_ref + kTau;
+        if (__builtin_amdgcn_ballot_w64(move)) {  // rare: re-reference the running state
+            const float m_new = move ? mx : m_ref;
+            const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
         float ls = 0.f;
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
@@ -234,10 +287,7 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
                 ls += p;
             }
         }
-        l_run = l_run * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+        l_run += ls;
 
         // O^T += V^T P^T over the 64 keys (4 k-blocks of 16).
         bf16x8 preg[4];
@@ -247,17 +297,23 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
             preg[2 * sub + 1] = pack_bf16x8(sacc[sub], 8);
         }
 #pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
+        for (int kb2 = 0; kb2 < 4; ++kb2) {
+            const int run = (kb2 * 16) * CPR * 16;  // first row of this k-block's 8-row runs
 #pragma unroll
-            for (int kb2 = 0; kb2 < 4; ++kb2) {
-                const bf16x8 vop =
-                    *reinterpret_cast<const bf16x8*>(Vt + (dblk * 32 + qi) * VSTR + kb2 * 16 + half * 8);
+            for (int dblk = 0; dblk < D / 32; ++dblk) {
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vst + run + voff[dblk]));
+                const s16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vst + run + 8 * CPR * 16 + voff[dblk]));
+                const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const bf16x8 vop = __builtin_bit_cast(bf16x8, both);
                 oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, preg[kb2], oacc[dblk], 0, 0, 0);
             }
         }
     }
 
-    const float l_tot = xhalf_sum(l_run);
+    // re-reference to the true row maximum
+    const float beta = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
+    const float l_tot = xhalf_sum(l_run) * beta;
     if (row < a.q_len) {
         const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + row;
         float* orow = a.o + idx * D;
@@ -265,19 +321,21 @@ __global__ __launch_bounds__(kThreads) void block_mfma_kernel(const BlockArgs a)
         for (int dblk = 0; dblk < D / 32; ++dblk) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 val = {oacc[dblk][4 * g], oacc[dblk][4 * g + 1], oacc[dblk][4 * g + 2],
-                                   oacc[dblk][4 * g + 3]};
+                const f32x4 val = {oacc[dblk][4 * g] * beta, oacc[dblk][4 * g + 1] * beta,
+                                   oacc[dblk][4 * g + 2] * beta, oacc[dblk][4 * g + 3] * beta};
                 *reinterpret_cast<f32x4*>(orow + dblk * 32 + 8 * g + 4 * half) = val;
             }
         }
         if (half == 0) {
-            a.m[idx] = (m_run == -INFINITY) ? -INFINITY : m_run * kLn2;
+            a.m[idx] = (m_true == -INFINITY) ? -INFINITY : m_true * kLn2;
             a.l[idx] = l_tot;
         }
     }
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kWaves = 8;
 
 }  // namespace
 
@@ -291,12 +349,15 @@ bool mfma_eligible(const BlockArgs& a, int dtype) {
 
 hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s) {
     if (a.q_len == 0) return hipSuccess;
+    constexpr int kMq = 32 * kWaves;
     const int n_qt = (a.q_len + kMq - 1) / kMq;
     const int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B;
     if (a.D == 128)
-        hipLaunchKernelGGL(block_mfma_kernel<128>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((block_mfma_kernel<128, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
+                           0, s, a);
     else
-        hipLaunchKernelGGL(block_mfma_kernel<64>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((block_mfma_kernel<64, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
+                           0, s, a);
     return hipGetLastError();
 }
 
