@@ -28,13 +28,14 @@
 // lane exactly its 8 V^T elements in the same key order.  V therefore stays
 // in its natural layout and moves HBM -> LDS untouched.
 //
-// Data movement.  K and V tiles (64 keys x head_dim) are copied HBM -> LDS by
-// global_load_lds_dwordx4 (no register staging), double buffered: the copy of
-// tile t+1 is issued before tile t is computed, one barrier per tile.  16-byte
-// chunk c of tile row r is stored at chunk position c ^ swz(r); swz permutes
-// the chunk positions of 8 consecutive rows so that the K operand reads (8
-// rows, one chunk) and the V^T transposed reads (4 rows, two adjacent chunks)
-// hit distinct LDS banks.
+// Data movement.  K and V tiles (kNk keys x head_dim) are copied HBM -> LDS by
+// global_load_lds_dwordx4 (no register staging) into separate double buffers
+// for K and for V.  16-byte chunk c of tile row r is stored at chunk position
+// c ^ swz(r).  gfx950's LDS serves 64 four-byte banks: swz is a bijection on
+// 16 consecutive rows (so the K operand reads -- 16 rows, one chunk -- use 16
+// distinct 16-byte bank groups) and gives 4 consecutive rows disjoint 4-chunk
+// spans (so the V^T transposed reads -- 4 rows x 4 chunks per 32 lanes -- are
+// conflict free).
 //
 // Online softmax.  The running maximum used as the exponent's reference is
 // only moved when a row's maximum grows by more than kTau (log2 units), so the
@@ -43,13 +44,18 @@
 // tracked separately and the partial is re-referenced to it once at the end,
 // so the emitted (m, l, o) are exactly the block's partial.
 //
-// Work decomposition: a workgroup of WAVES waves owns 32*WAVES query rows of
-// one (b, q-head); each wave owns 32 rows.  Causal masking uses the block's
-// mask offset: tiles past the last visible key are never loaded, waves with no
-// visible key in a tile skip it, and the element mask is applied only on
-// tiles that straddle the diagonal (or the ragged end of the block).  Tiles
-// are dispatched heaviest first and grouped so that one head's workgroups land
-// on the same XCD (shared L2 for K/V).
+// Work decomposition: a workgroup of WAVES (8) waves owns 32*WAVES query rows
+// of one (b, q-head); each wave owns 32 rows.  Keys are visited in tiles of
+// kNk.  Waves w and w + 4 share a SIMD; they form two groups run half a tile
+// apart ("ping-pong"), so while one wave of a SIMD issues MFMAs (the PV
+// product of the previous tile, then QK^T of the current one) the other runs
+// its softmax on the vector ALU.  Each MFMA half is one software-pipelined
+// stream in which every operand's LDS read is issued a few MFMAs ahead of its
+// use.  Causal masking uses the block's mask offset: tiles past the
+// workgroup's last visible key are never loaded, and the element mask is
+// applied only on tiles that straddle the diagonal (or the ragged end of the
+// block).  Tiles are dispatched heaviest first and grouped so that one head's
+// workgroups land on the same XCD (shared L2 for K/V).
 #include <cmath>
 
 #include "ra_internal.h"
@@ -65,15 +71,39 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) short s16x8;
 
-constexpr int kNk = 64;  // keys per tile
+// Compile-time tuning knobs (defaults are the measured best on gfx950).
+#ifndef RA_MFMA_NK
+#define RA_MFMA_NK 128
+#endif
+#ifndef RA_MFMA_WAVES
+#define RA_MFMA_WAVES 8
+#endif
+#ifndef RA_MFMA_SETPRIO
+#define RA_MFMA_SETPRIO 1
+#endif
+#ifndef RA_MFMA_PINGPONG
+#define RA_MFMA_PINGPONG 1
+#endif
+#ifndef RA_MFMA_PREFETCH
+#define RA_MFMA_PREFETCH 4
+#endif
+constexpr int kNk = RA_MFMA_NK;  // keys per tile (64 or 128)
+constexpr int kSub = kNk / 32;   // 32-key sub-tiles per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)((char*)(p)))
+typedef __attribute__((address_space(3))) char lds_char;
 
-// Chunk-position permutation of the 8 rows r, r+1, ... (r % 8 == 0).
-__device__ inline int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Chunk-position permutation of tile rows (see the data-movement note).
+// D = 128: 16 chunks a row, swap the two 2-bit fields of r & 15.
+// D = 64: 8 chunks a row (two rows per 64-bank line), bits 1..3 of r.
+template <int D>
+__device__ inline int swz(int r) {
+    if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
 
 // Combine a lane's value with lane ^ 32's (v_permlane32_swap exchanges halves).
 __device__ inline float xhalf_max(float x) {
@@ -115,25 +145,30 @@ __device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // compiler's wait-count pass does not treat the prefetch of the next tile as a
 // hazard for reads of the current one; completion is awaited explicitly
 // (wait_vmem_all) before the barrier that publishes a tile.
-__device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
+// The address is a wave-uniform base (SGPR pair) plus a 32-bit per-lane
+// byte offset, so no per-lane 64-bit arithmetic is needed.
+__device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_base) {
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, off"
+        "global_load_lds_dwordx4 %0, %1"
         :
-        : "v"(src), "s"(lds_base)
+        : "v"(offset), "s"(base), "s"(lds_base)
         : "memory", "m0");
 }
 
+// Two waves per SIMD (<= 256 registers): one wave's MFMAs overlap the other's
+// softmax arithmetic.
 template <int D, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs a) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_mfma_kernel(
+    const BlockArgs a) {
     constexpr int kMq = 32 * WAVES;
     constexpr int CPR = D / 8;                 // 16-byte chunks per tile row
     constexpr int TILE_BYTES = kNk * D * 2;    // one K (or V) tile
     constexpr int INSTR = TILE_BYTES / 1024;   // 1 KiB copy instructions per tile
     constexpr int PER_WAVE = INSTR / WAVES;
     static_assert(INSTR % WAVES == 0, "tile copy must split evenly over waves");
-    __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * TILE_BYTES];  // [stage][K, V]
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];  // K0, K1, V0, V1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -183,40 +218,60 @@ __global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs 
         }
     }
 
-    // Copy of tile t into stage s: instruction i of this wave fills LDS chunk
-    // positions [64 i', 64 i' + 64) of the K and V tiles (i' = wave-major index);
-    // each lane fetches the global chunk that belongs at its position.  Rows past
-    // the block re-read its last row (finite values; they are masked).
+    // Tile copies.  K tiles live in LDS buffers 0/1, V tiles in buffers 2/3.
+    // Instruction i of this wave fills chunk positions [64 i', 64 i' + 64) of a
+    // tile (i' = wave-major instruction index); each lane fetches the global
+    // chunk that belongs at its position.  Rows past the block re-read its last
+    // row (finite values; they are masked).
     const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
-    auto issue_tile = [&](int t, int s) {
-        const uint32_t kdst = lds0 + s * 2 * TILE_BYTES;
-        const uint32_t vdst = kdst + TILE_BYTES;
+    // per-lane byte offsets of this wave's copy instructions within a full tile
+    uint32_t kcp[PER_WAVE], vcp[PER_WAVE];
+    int crow[PER_WAVE], cchunk[PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < PER_WAVE; ++i) {
-            const int inst = wave * PER_WAVE + i;
-            const int pos = inst * 64 + lane;
-            const int r = pos / CPR;
-            const int c = (pos % CPR) ^ swz(r);
-            const int key = min(t * kNk + r, a.kv_len - 1);
-            lds_dma16(kp + key * ks2 + c * 8, kdst + inst * 1024);
-            lds_dma16(vp + key * vs2 + c * 8, vdst + inst * 1024);
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int pos = (wave * PER_WAVE + i) * 64 + lane;
+        crow[i] = pos / CPR;
+        cchunk[i] = (pos % CPR) ^ swz<D>(crow[i]);
+        kcp[i] = static_cast<uint32_t>(crow[i] * ks2 * 2 + cchunk[i] * 16);
+        vcp[i] = static_cast<uint32_t>(crow[i] * vs2 * 2 + cchunk[i] * 16);
+    }
+    auto issue_copy = [&](const uint16_t* src, int64_t stride, const uint32_t* off, int t, int buf)
+                          __attribute__((always_inline)) {
+        const uint16_t* base = src + static_cast<int64_t>(t) * kNk * stride;
+        const uint32_t dst = lds0 + buf * TILE_BYTES;
+        const int last = a.kv_len - 1 - t * kNk;  // last valid row of this tile
+        if (last >= kNk - 1) {
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) lds_dma16(base, off[i], dst + (wave * PER_WAVE + i) * 1024);
+        } else {  // ragged end of the block: rows past it re-read its last row (masked later)
+#pragma unroll
+            for (int i = 0; i < PER_WAVE; ++i) {
+                const uint32_t o = static_cast<uint32_t>(min(crow[i], last) * stride * 2 + cchunk[i] * 16);
+                lds_dma16(base, o, dst + (wave * PER_WAVE + i) * 1024);
+            }
         }
     };
+    auto issue_k = [&](int t) __attribute__((always_inline)) { issue_copy(kp, ks2, kcp, t, t & 1); };
+    auto issue_v = [&](int t) __attribute__((always_inline)) { issue_copy(vp, vs2, vcp, t, 2 + (t & 1)); };
 
     // per-lane LDS byte offsets of the operand reads
-    const int sq = swz(qi);  // K rows sub*32 + qi share swz(qi)
-    int koff[D / 16];
+    const lds_char* lds = LDS_PTR(char, smem);
+    const int sq = swz<D>(qi);  // K rows sub*32 + qi share swz(qi)
+    uint32_t koff[D / 16];
 #pragma unroll
     for (int kb = 0; kb < D / 16; ++kb) koff[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
     const int j = lane & 15;                        // lane within its 16-lane group
     const int dsub = (lane >> 4) & 1;               // which 16 columns of a 32-column block
-    const int vrow = 4 * half + (j >> 2);           // row within an 8-row run
-    const int sv = swz(vrow);
-    int voff[D / 32];
+    const int vrow = 4 * half + (j >> 2);           // row within a 16-row k-block (first run)
+    const int sv_lo = swz<D>(vrow), sv_hi = swz<D>(vrow + 8);
+    uint32_t voff_lo[D / 32], voff_hi[D / 32];
 #pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk)
-        voff[dblk] = (vrow * CPR + ((4 * dblk + 2 * dsub + ((j & 3) >> 1)) ^ sv)) * 16 + (j & 1) * 8;
+    for (int dblk = 0; dblk < D / 32; ++dblk) {
+        const int c = 4 * dblk + 2 * dsub + ((j & 3) >> 1);
+        voff_lo[dblk] = (vrow * CPR + (c ^ sv_lo)) * 16 + (j & 1) * 8;
+        voff_hi[dblk] = ((vrow + 8) * CPR + (c ^ sv_hi)) * 16 + (j & 1) * 8;
+    }
 
     const float c2 = a.scale * kLog2e;  // exp(s*scale) = exp2(s*c2)
     f32x16 oacc[D / 32];
@@ -225,47 +280,38 @@ __global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs 
     float m_ref = -INFINITY;   // exponent reference (log2 units of the scaled score)
     float m_true = -INFINITY;  // running row maximum
     float l_run = 0.f;         // this lane's share of the running sum
+    f32x16 sacc[kSub];         // S^T of the current tile, then its probabilities
+    bf16x8 preg[2 * kSub];     // P^T operand of the tile awaiting its PV product
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int t = 0; t < n_tiles; ++t) {
+    auto visible = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < n_tiles && t * kNk < wave_key_end; };
+
+    // mask, row max, reference move, exponentials, row sum, bf16 P^T.
+    auto softmax = [&](int t) __attribute__((always_inline)) {
         const int kbase = t * kNk;
-        wait_vmem_all();
-        __syncthreads();
-        if (t + 1 < n_tiles) issue_tile(t + 1, (t + 1) & 1);
-        if (kbase >= wave_key_end) continue;  // nothing visible to this wave here
-        const char* kst = smem + (t & 1) * 2 * TILE_BYTES;
-        const char* vst = kst + TILE_BYTES;
-
-        // S^T = K Q^T for two 32-key sub-tiles.
-        f32x16 sacc[2];
+        // mask (diagonal / ragged tiles only) and row max, on the raw scores:
+        // the scale is positive, so it is applied once, to the maximum.
+        if (kbase + kNk > wave_full_end) {
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            sacc[sub] = f32x16{};
+            for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kst + sub * 32 * CPR * 16 + koff[kb]);
-                sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[kb], sacc[sub], 0, 0, 0);
-            }
-        }
-
-        // scale, mask (diagonal / ragged tiles only), row max
-        const bool need_mask = kbase + kNk > wave_full_end;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float s = sacc[sub][v] * c2;
-                if (need_mask) {
+                for (int v = 0; v < 16; ++v) {
                     const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
                     const bool vis = key < a.kv_len && (!a.causal || key <= row + a.mask_offset);
-                    s = vis ? s : -INFINITY;
+                    sacc[sub][v] = vis ? sacc[sub][v] : -INFINITY;
                 }
-                sacc[sub][v] = s;
-                mx = fmaxf(mx, s);
             }
         }
-        mx = xhalf_max(mx);
+        // row max as a balanced tree (short dependency chains)
+        float mt[8 * kSub];
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) mt[8 * sub + v] = fmaxf(sacc[sub][2 * v], sacc[sub][2 * v + 1]);
+#pragma unroll
+        for (int w = 4 * kSub; w >= 1; w >>= 1)
+#pragma unroll
+            for (int v = 0; v < w; ++v) mt[v] = fmaxf(mt[v], mt[v + w]);
+        const float mx = xhalf_max(mt[0]) * c2;
         m_true = fmaxf(m_true, mx);
         const bool move = mx > m_ref + kTau;
         if (__builtin_amdgcn_ballot_w64(move)) {  // rare: re-reference the running state
@@ -276,40 +322,157 @@ __global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs 
             for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
             m_ref = m_new;
         }
-        const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-        float ls = 0.f;
+        const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(sacc[sub][v] - m_use);
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][v], c2, neg_m));
                 sacc[sub][v] = p;
-                ls += p;
+                ls[v & 3] += p;
             }
         }
-        l_run += ls;
-
-        // O^T += V^T P^T over the 64 keys (4 k-blocks of 16).
-        bf16x8 preg[4];
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
+        for (int sub = 0; sub < kSub; ++sub) {
             preg[2 * sub] = pack_bf16x8(sacc[sub], 0);
             preg[2 * sub + 1] = pack_bf16x8(sacc[sub], 8);
         }
-#pragma unroll
-        for (int kb2 = 0; kb2 < 4; ++kb2) {
-            const int run = (kb2 * 16) * CPR * 16;  // first row of this k-block's 8-row runs
-#pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk) {
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vst + run + voff[dblk]));
-                const s16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vst + run + 8 * CPR * 16 + voff[dblk]));
+    };
+
+    // One MFMA half as a software-pipelined operand stream: the PV MFMAs of
+    // tile tp (O^T += V^T P^T, 4-k-block x dblk order) then the QK^T MFMAs of
+    // tile tq (kb-major, sub-tile-minor).  Each operand's LDS read is issued
+    // kPf steps before its MFMA, and a scheduling fence after every step keeps
+    // that distance, so LDS latency hides behind the MFMAs in flight.
+    constexpr int kPf = RA_MFMA_PREFETCH;
+    constexpr int NPV = 2 * kSub * (D / 32), NQK = kSub * (D / 16), NT = NPV + NQK;
+    auto mfma_stream = [&]<bool PV, bool QK>(int tp, int tq) __attribute__((always_inline)) {
+        constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NT : NPV, N = I1 - I0;
+        const lds_char* vst = lds + (2 + (tp & 1)) * TILE_BYTES;
+        const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
+        auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+            if (i < NPV) {
+                const int kb2 = i / (D / 32), dblk = i % (D / 32);
+                const int run = (kb2 * 16) * CPR * 16;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vst + voff_lo[dblk] + run));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vst + voff_hi[dblk] + run));
                 const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                const bf16x8 vop = __builtin_bit_cast(bf16x8, both);
-                oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, preg[kb2], oacc[dblk], 0, 0, 0);
+                return __builtin_bit_cast(bf16x8, both);
             }
+            const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
+            return *(const __attribute__((address_space(3))) bf16x8*)(kst + koff[kb] + sub * 32 * CPR * 16);
+        };
+        auto run_mfma = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+            if (i < NPV) {
+                const int kb2 = i / (D / 32), dblk = i % (D / 32);
+                oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, preg[kb2], oacc[dblk], 0, 0, 0);
+            } else {
+                const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
+                sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kb], kb == 0 ? f32x16{} : sacc[sub], 0,
+                                                                     0, 0);
+            }
+        };
+        bf16x8 ops[kPf];
+#pragma unroll
+        for (int n = 0; n < kPf && n < N; ++n) ops[n] = load_op(I0 + n);
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const bf16x8 op = ops[n % kPf];
+            if (n + kPf < N) ops[n % kPf] = load_op(I0 + n + kPf);
+            run_mfma(I0 + n, op);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+#if RA_MFMA_PINGPONG
+    // Two groups of WAVES/2 waves (one wave per SIMD each), half a tile apart.
+    // Between consecutive barriers one group runs MFMAs (PV of tile t-1, then
+    // QK^T of tile t) while the other runs the softmax of its current tile, so
+    // each SIMD's matrix core and vector ALU work at the same time.  K(t+1)
+    // and V(t) are copied during iteration t and published by its final
+    // barrier; a buffer is refilled only after the barrier that ends its last
+    // reader's phase.
+    static_assert(WAVES % 8 == 0, "ping-pong needs two groups of one wave per SIMD");
+    const int group = wave / (WAVES / 2);
+    // The MFMA half always runs the full stream: for a tile this wave cannot
+    // see, P is zero (valu_half) and the V buffers hold finite values (zeroed
+    // below before any copy), so the PV product adds exactly zero, and scores
+    // of an unseen tile are never read.  A group's phase lasts as long as its
+    // slowest wave, so skipping would not shorten it.
+    auto mfma_half = [&](int t) __attribute__((always_inline)) {
+        if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+        mfma_stream.template operator()<true, true>(t - 1, t);
+        if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+    auto valu_half = [&](int t) __attribute__((always_inline)) {
+        if (visible(t)) {
+            softmax(t);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * kSub; ++i) preg[i] = bf16x8{};
+        }
+    };
+    // Both groups run the same loop body -- MFMA half of tile t, barrier,
+    // softmax half of tile t, barrier -- but group 1 first passes one extra
+    // barrier (and group 0 one at the end), so group 1 runs one phase behind.
+    // Global phase 2t carries group 0's MFMA half of tile t and group 1's
+    // softmax half of tile t-1; phase 2t+1 the other way round.  The copies of
+    // K(t+1) and V(t) start in phase 2t (each group issues its share from the
+    // half that falls there) and are awaited at the end of phase 2t+1.
+    if (n_tiles > 0) {
+        // finite V buffers and P^T = 0 before the first PV product
+        for (int i = tid; i < 2 * TILE_BYTES / 16; i += 64 * WAVES)
+            *(__attribute__((address_space(3))) s16x8*)(lds + 2 * TILE_BYTES + i * 16) = s16x8{};
+#pragma unroll
+        for (int i = 0; i < 2 * kSub; ++i) preg[i] = bf16x8{};
+        issue_k(0);
+        wait_vmem_all();
+        __syncthreads();
+        if (group == 1) {
+            if (1 < n_tiles) issue_k(1);
+            issue_v(0);
+            __syncthreads();
+        }
+        for (int t = 0; t <= n_tiles; ++t) {
+            if (group == 0) {
+                if (t + 1 < n_tiles) issue_k(t + 1);
+                if (t < n_tiles) issue_v(t);
+            }
+            mfma_half(t);
+            if (group == 1) wait_vmem_all();
+            __syncthreads();
+            if (group == 1) {
+                if (t + 2 < n_tiles) issue_k(t + 2);
+                if (t + 1 < n_tiles) issue_v(t + 1);
+            }
+            valu_half(t);
+            if (group == 0) wait_vmem_all();
+            __syncthreads();
+        }
+        if (group == 0) __syncthreads();
     }
+#else
+    if (n_tiles > 0) {
+        issue_k(0);
+        issue_v(0);
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+        wait_vmem_all();
+        __syncthreads();
+        if (t + 1 < n_tiles) {
+            issue_k(t + 1);
+            issue_v(t + 1);
+        }
+        if (!visible(t)) continue;  // nothing visible to this wave here
+        mfma_stream.template operator()<false, true>(t, t);
+        softmax(t);
+        mfma_stream.template operator()<true, false>(t, t);
+    }
+#endif
 
     // re-reference to the true row maximum
     const float beta = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
@@ -335,7 +498,7 @@ __global__ __launch_bounds__(64 * WAVES) void block_mfma_kernel(const BlockArgs 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int kWaves = 8;
+constexpr int kWaves = RA_MFMA_WAVES;
 
 }  // namespace
 
