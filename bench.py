@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="fold each block's partial with a separate merge launch instead of in the block kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring positions are virtual positions on a single "
@@ -165,7 +167,8 @@ def main():
     o_sh = torch.empty_like(q_sh)
     lse = torch.empty(q_sh.shape[:4], dtype=torch.float32, device=dev)
     o_full = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=dev) if q_g is not None else None
-    desc = ra.ring_desc(q_sh, k_sh, n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"])
+    desc = ra.ring_desc(q_sh, k_sh, n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"],
+                        separate_merge=args.separate_merge)
     workspace = torch.empty(ra.ra_ring_workspace_size(desc), dtype=torch.uint8, device=dev)
 
     def step(stats):
@@ -174,7 +177,8 @@ def main():
         if q_g is not None:
             ra.ra_stripe_permute(q_g, q_sh, layout=lay, inverse=False, n_pos=N)
         st = ra.ra_ring_forward(q_sh, k_sh, v_sh, o_sh, lse, n_pos=N, first_pos=first, layout=lay,
-                                causal=cfg["causal"], workspace=workspace, stats=stats)
+                                causal=cfg["causal"], workspace=workspace, stats=stats,
+                                separate_merge=args.separate_merge)
         if o_full is not None:
             ra.ra_stripe_permute(o_sh, o_full, layout=lay, inverse=True, n_pos=N)
         return st
@@ -207,17 +211,19 @@ def main():
                 "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",
                 "launches": totals["block_launches"], "mean_launch_ms": round(per_launch_ms, 4)}
 
-    # merge kernel: algorithmic bytes per step.  Per position with c computed
-    # blocks: c - 2 plain folds (read two partials, write one: 12 D + 24 bytes a
-    # row) and one fold that finalises (read two partials, write the bf16 output
-    # and the log-sum-exp: 8 D + 16 + 2 D + 4 bytes a row); c = 1 finalises only.
+    # merge kernel: algorithmic bytes per step.  Fused schedule (default): the
+    # block kernel folds each partial into the running state, and the merge
+    # kernel only finalises (read fp32 O, m, l; write the bf16 output and the
+    # log-sum-exp: 4 D + 8 + 2 D + 4 bytes a row).  Separate schedule: per
+    # position with c computed blocks, c - 2 plain folds (read two states, write
+    # one: 12 D + 24 bytes a row) and one fold that finalises (8 D + 16 + 2 D + 4).
     rows_pos = B * Hq * sb
     merge_bytes = 0
     for p in range(n_run):
         c = sum(1 for j in range(N)
                 if not (cfg["causal"] and ra.ra_unmasked_pairs(
                     sb, sb, True, ra.ra_ring_pair_offset(lay, N, sb, first + p, j)) == 0))
-        if c == 1:
+        if c == 1 or not args.separate_merge:
             merge_bytes += rows_pos * (4 * D + 8 + 2 * D + 4)
         else:
             merge_bytes += (c - 2) * rows_pos * (12 * D + 24) + rows_pos * (8 * D + 16 + 2 * D + 4)
@@ -244,6 +250,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
                    "head_dim": D, "ring_positions": N, "layout": lay, "causal": cfg["causal"],
                    "positions_run": n_run, "first_position": first,
+                   "merge_schedule": "separate" if args.separate_merge else "fused",
                    "unmasked_flops_per_step": flops_per_step},
         "roofline": roofline, "merge": merge, "cpu_baseline": cpu,
     }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 1
+#define RA_ABI_VERSION 2
 
 typedef enum ra_status {
     RA_OK = 0,
@@ -66,6 +66,7 @@ typedef enum ra_layout { RA_CONTIGUOUS = 0, RA_STRIPED = 1 } ra_layout;
 
 /* ra_block_desc.flags */
 #define RA_BLOCK_FORCE_SIMT 1u /* use the vector-ALU kernel even where the MFMA kernel applies */
+#define RA_BLOCK_ACCUMULATE 2u /* (o, m, l) hold a running state on entry; see ra_block_attn_fwd */
 
 /*
  * One query block against one key/value block.
@@ -115,6 +116,12 @@ typedef struct ra_block_desc {
  */
 ra_status ra_block_attn_fwd(const ra_block_desc* desc, const void* q, const void* k,
                             const void* v, float* o, float* m, float* l, void* stream);
+/* With RA_BLOCK_ACCUMULATE, (o, m, l) hold a running state (a partial of some
+ * other key set, in the same layout) on entry, and on return hold the merge of
+ * that state with this block's partial -- the result ra_lse_merge would give
+ * for (running state, this partial), computed in the kernel's epilogue without
+ * writing the partial out.  The running state must be initialised (e.g. by a
+ * call without the flag, or to m = -inf, l = 0, o = 0). */
 
 /*
  * ra_lse_merge -- combine two partials with the running softmax ("Ring
@@ -176,6 +183,12 @@ typedef struct ra_ring_desc {
                                 a copy stream, ordered by HIP events, as a ring
                                 transfer would be                              */
     int32_t n_streams;  /* compute streams; 0 = min(n_run, 8)                     */
+    int32_t separate_merge; /* 0: each step after a position's first merges its
+                               partial into the running state inside the block
+                               kernel (RA_BLOCK_ACCUMULATE) and one finalising
+                               ra_lse_merge pass ends the position;
+                               1: each step writes a partial and ra_lse_merge
+                               folds it in (the last fold also finalises)     */
     const int32_t* visit_order; /* host array [n_pos] (a permutation) or NULL     */
     ra_ring_stats* stats;       /* host pointer or NULL.  When set, every launch is
                                    timed with HIP events and the call waits for
@@ -190,9 +203,10 @@ ra_status ra_ring_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * ra_ring_forward -- the ring schedule of "Ring Attention", section "How ring
  * attention works", for N virtual positions on one GPU: no inter-GPU transfer,
  * no collective, no sharding.  Per position, the first computed step writes
- * its partial straight into the running state, every later step computes a
- * partial with ra_block_attn_fwd's kernel and folds it in with
- * ra_lse_merge's kernel, and the last fold also finalises.  Fully masked
+ * its partial straight into the running state; every later step merges its
+ * block into that state (in the block kernel, or -- with separate_merge -- by
+ * a partial plus an ra_lse_merge fold); a final ra_lse_merge pass normalises
+ * (fused schedule) or the last fold does (separate schedule).  Fully masked
  * (position, block) pairs are skipped (contiguous causal: blocks after the
  * query block).  Positions are spread over n_streams library-owned streams.
  *

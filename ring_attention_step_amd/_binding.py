@@ -19,6 +19,7 @@ RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE = range(
 RA_F32, RA_BF16 = 0, 1
 RA_CONTIGUOUS, RA_STRIPED = 0, 1
 RA_BLOCK_FORCE_SIMT = 1
+RA_BLOCK_ACCUMULATE = 2
 LAYOUTS = {"contiguous": RA_CONTIGUOUS, "striped": RA_STRIPED}
 
 
@@ -50,6 +51,7 @@ class ra_ring_desc(ctypes.Structure):
                 ("n_run", ctypes.c_int32), ("layout", ctypes.c_int32), ("block_len", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("emulate_copy", ctypes.c_int32), ("n_streams", ctypes.c_int32),
+                ("separate_merge", ctypes.c_int32),
                 ("visit_order", ctypes.POINTER(ctypes.c_int32)),
                 ("stats", ctypes.POINTER(ra_ring_stats))]
 
@@ -211,7 +213,7 @@ def ra_lse_merge(o_acc, m_acc, l_acc, o_part=None, m_part=None, l_part=None, o_o
 
 
 def ring_desc(q, k, *, n_pos, first_pos=0, layout="contiguous", causal=False, scale=0.0, emulate_copy=False,
-              n_streams=0, visit_order=None, stats=None):
+              n_streams=0, separate_merge=False, visit_order=None, stats=None):
     """ra_ring_desc for q [n_run, B, Hq, Sb, D] and k [n_pos, B, Hkv, Sb, D]."""
     n_run, B, Hq, Sb, D = q.shape
     if k.shape[0] != n_pos or k.shape[1] != B or k.shape[3] != Sb or k.shape[4] != D:
@@ -222,6 +224,7 @@ def ring_desc(q, k, *, n_pos, first_pos=0, layout="contiguous", causal=False, sc
     d.layout = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     d.block_len, d.dtype, d.causal, d.scale = Sb, _dtype(q), int(bool(causal)), float(scale)
     d.emulate_copy, d.n_streams = int(bool(emulate_copy)), int(n_streams)
+    d.separate_merge = int(bool(separate_merge))
     if visit_order is not None:
         arr = (ctypes.c_int32 * n_pos)(*[int(x) for x in visit_order])
         d._order_keepalive = arr
@@ -238,8 +241,8 @@ def ra_ring_workspace_size(desc) -> int:
 
 
 def ra_ring_forward(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contiguous", causal=False,
-                    scale=0.0, emulate_copy=False, n_streams=0, visit_order=None, workspace=None,
-                    stats=False, stream=None):
+                    scale=0.0, emulate_copy=False, n_streams=0, separate_merge=False, visit_order=None,
+                    workspace=None, stats=False, stream=None):
     """Run positions first_pos .. first_pos + n_run - 1 of an n_pos ring on one GPU.
 
     Returns a dict of ra_ring_stats when stats=True (the call then waits for its
@@ -252,7 +255,8 @@ def ra_ring_forward(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contigu
         raise ValueError("v must match k and o must match q")
     st = ra_ring_stats() if stats else None
     d = ring_desc(q, k, n_pos=n_pos, first_pos=first_pos, layout=layout, causal=causal, scale=scale,
-                  emulate_copy=emulate_copy, n_streams=n_streams, visit_order=visit_order, stats=st)
+                  emulate_copy=emulate_copy, n_streams=n_streams, separate_merge=separate_merge,
+                  visit_order=visit_order, stats=st)
     need = ra_ring_workspace_size(d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -474,24 +474,43 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     }
 #endif
 
-    // re-reference to the true row maximum
-    const float beta = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
-    const float l_tot = xhalf_sum(l_run) * beta;
+    // Epilogue.  The partial (oacc, l_run) is referenced to exp2(m_ref); its
+    // row maximum is m_true.  Written as is (re-referenced to m_true), or --
+    // with a.accumulate -- merged into the running state (o, m, l) of the row
+    // with the same online-softmax rule as ra_lse_merge:
+    //   m = max(m_a, m_p);  w_x = exp(m_x - m) (0 if m_x = -inf).
+    const float l_ref = xhalf_sum(l_run);
     if (row < a.q_len) {
         const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + row;
         float* orow = a.o + idx * D;
+        float m_out = m_true;  // log2 units
+        float wa = 0.f, l_a = 0.f;
+        float wp = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
+        if (a.accumulate) {
+            const float m_a = a.m[idx] * kLog2e;  // -inf stays -inf
+            l_a = a.l[idx];
+            m_out = fmaxf(m_a, m_true);
+            wa = (m_a == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_a - m_out);
+            wp = (m_true == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_out);
+        }
 #pragma unroll
         for (int dblk = 0; dblk < D / 32; ++dblk) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 val = {oacc[dblk][4 * g] * beta, oacc[dblk][4 * g + 1] * beta,
-                                   oacc[dblk][4 * g + 2] * beta, oacc[dblk][4 * g + 3] * beta};
-                *reinterpret_cast<f32x4*>(orow + dblk * 32 + 8 * g + 4 * half) = val;
+                f32x4* dst = reinterpret_cast<f32x4*>(orow + dblk * 32 + 8 * g + 4 * half);
+                f32x4 val = {oacc[dblk][4 * g] * wp, oacc[dblk][4 * g + 1] * wp, oacc[dblk][4 * g + 2] * wp,
+                             oacc[dblk][4 * g + 3] * wp};
+                if (a.accumulate) {
+                    const f32x4 prev = *dst;
+                    val = {__builtin_fmaf(wa, prev[0], val[0]), __builtin_fmaf(wa, prev[1], val[1]),
+                           __builtin_fmaf(wa, prev[2], val[2]), __builtin_fmaf(wa, prev[3], val[3])};
+                }
+                *dst = val;
             }
         }
         if (half == 0) {
-            a.m[idx] = (m_true == -INFINITY) ? -INFINITY : m_true * kLn2;
-            a.l[idx] = l_tot;
+            a.m[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
+            a.l[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
         }
     }
 }

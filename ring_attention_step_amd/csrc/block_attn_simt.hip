@@ -145,19 +145,34 @@ __global__ __launch_bounds__(256) void block_simt_kernel(const BlockArgs a) {
         }
     }
 
+    // Epilogue: write the partial, or (a.accumulate) merge it into the row's
+    // running state (o, m, l) with the online-softmax rule of ra_lse_merge.
 #pragma unroll
     for (int rr = 0; rr < kRowsPerWave; ++rr) {
         const int r = r0 + wave * kRowsPerWave + rr;
         if (r >= a.q_len) break;
         const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + r;
+        float m_out = m_run[rr], wa = 0.f, wp = 1.f, l_a = 0.f;
+        if (a.accumulate) {
+            const float m_a = a.m[idx];
+            l_a = a.l[idx];
+            m_out = fmaxf(m_a, m_run[rr]);
+            wa = (m_a == -INFINITY) ? 0.f : expf(m_a - m_out);
+            wp = (m_run[rr] == -INFINITY) ? 0.f : expf(m_run[rr] - m_out);
+        }
 #pragma unroll
         for (int t = 0; t < kColsPerLane; ++t) {
             const int j = lane + 64 * t;
-            if (j < D) a.o[idx * D + j] = acc[rr][t];
+            if (j < D) {
+                float val = acc[rr][t] * wp;
+                if (a.accumulate) val = fmaf(wa, a.o[idx * D + j], val);
+                a.o[idx * D + j] = val;
+            }
         }
+        __builtin_amdgcn_wave_barrier();  // every lane has read (m, l) before lane 0 writes them
         if (lane == 0) {
-            a.m[idx] = m_run[rr];
-            a.l[idx] = l_run[rr];
+            a.m[idx] = m_out;
+            a.l[idx] = fmaf(wa, l_a, wp * l_run[rr]);
         }
     }
 }

@@ -125,7 +125,8 @@ ra_status ra_block_attn_fwd(const ra_block_desc* d, const void* q, const void* k
     if (d->q_len < 0 || d->kv_len < 0 || d->q_len > kMaxLen || d->kv_len > kMaxLen)
         return fail(RA_ERR_INVALID, "q_len / kv_len out of range");
     if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID, "causal must be 0 or 1");
-    if (d->flags & ~RA_BLOCK_FORCE_SIMT) return fail(RA_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+    if (d->flags & ~(RA_BLOCK_FORCE_SIMT | RA_BLOCK_ACCUMULATE))
+        return fail(RA_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
     if (d->pos_stride < 1) return fail(RA_ERR_INVALID, "pos_stride must be >= 1");
     if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
     for (int i = 0; i < 3; ++i)
@@ -160,6 +161,7 @@ ra_status ra_block_attn_fwd(const ra_block_desc* d, const void* q, const void* k
     a.scale = resolve_scale(d->scale, d->head_dim);
     a.causal = d->causal;
     a.mask_offset = clamp_offset(ra_mask_offset(d->q_pos0, d->k_pos0, d->pos_stride), d->q_len, d->kv_len);
+    a.accumulate = (d->flags & RA_BLOCK_ACCUMULATE) ? 1 : 0;
     return launch_block(a, d->dtype, d->flags, static_cast<hipStream_t>(stream));
 }
 
@@ -240,6 +242,7 @@ ra_status check_ring(const ra_ring_desc* d) {
     if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID, "causal must be 0 or 1");
     if (d->emulate_copy != 0 && d->emulate_copy != 1) return fail(RA_ERR_INVALID, "emulate_copy must be 0 or 1");
     if (d->n_streams < 0 || d->n_streams > 64) return fail(RA_ERR_INVALID, "n_streams must be in [0, 64]");
+    if (d->separate_merge != 0 && d->separate_merge != 1) return fail(RA_ERR_INVALID, "separate_merge must be 0 or 1");
     if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
     if (d->visit_order) {
         std::vector<char> seen(d->n_pos, 0);
@@ -261,8 +264,8 @@ RingGeometry geometry(const ra_ring_desc* d) {
     g.n_streams = d->n_streams > 0 ? std::min(d->n_streams, d->n_run) : std::min(d->n_run, 8);
     g.acc_o = round_up(static_cast<size_t>(g.q_elems) * 4, 256);
     g.acc_ml = round_up(static_cast<size_t>(g.rows) * 4, 256);
-    g.part_o = g.acc_o;
-    g.part_ml = g.acc_ml;
+    g.part_o = d->separate_merge ? g.acc_o : 0;  // per-stream partials only for the separate schedule
+    g.part_ml = d->separate_merge ? g.acc_ml : 0;
     g.slot = d->emulate_copy ? round_up(static_cast<size_t>(g.kv_elems) * elem_size(d->dtype), 256) : 0;
     // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: partial o, m, l
     g.total = static_cast<size_t>(d->n_run) * (g.acc_o + 2 * g.acc_ml + 4 * g.slot) +
@@ -485,13 +488,16 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                 if (d->emulate_copy) RA_HIP(hipStreamWaitEvent(cs, ev_copied(p, par), 0));
                 const bool first = done[p] == 0;
                 const bool last = done[p] + 1 == n_computed[p];
+                const bool fused = !d->separate_merge;
                 ra::BlockArgs a{};
                 a.q = qbase + static_cast<size_t>(p) * g.q_elems * es;
                 a.k = kp;
                 a.v = vp;
-                a.o = first ? pos[p].o : part[sid].o;
-                a.m = first ? pos[p].m : part[sid].m;
-                a.l = first ? pos[p].l : part[sid].l;
+                const bool into_acc = first || fused;
+                a.o = into_acc ? pos[p].o : part[sid].o;
+                a.m = into_acc ? pos[p].m : part[sid].m;
+                a.l = into_acc ? pos[p].l : part[sid].l;
+                a.accumulate = (fused && !first) ? 1 : 0;
                 a.B = d->batch;
                 a.Hq = d->q_heads;
                 a.Hkv = d->kv_heads;
@@ -518,14 +524,14 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                     RA_HIP(hipEventRecord(ev_used(p, par), cs));
                     used_parity[2 * p + par] = 1;
                 }
-                if (!first || last) {
+                if ((!first && !fused) || last) {
                     ra::MergeArgs ma{};
                     ma.rows = g.rows;
                     ma.D = D;
                     ma.o_acc = pos[p].o;
                     ma.m_acc = pos[p].m;
                     ma.l_acc = pos[p].l;
-                    if (!first) {
+                    if (!first && !fused) {
                         ma.o_p = part[sid].o;
                         ma.m_p = part[sid].m;
                         ma.l_p = part[sid].l;

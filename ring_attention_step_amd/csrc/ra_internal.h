@@ -25,6 +25,8 @@ struct BlockArgs {
     float scale;                  // softmax scale (already resolved)
     int32_t causal;
     int32_t mask_offset;  // key c visible to row r iff c <= r + mask_offset
+    int32_t accumulate;   // 0: write the block's partial to (o, m, l);
+                          // 1: (o, m, l) hold a running state; merge the partial into it
 };
 
 // Vector-ALU kernel: binary32 or bfloat16 inputs, any D in [1, 256], fp32 math.

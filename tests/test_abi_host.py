@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     for name in names:
         assert hasattr(lib, name), f"libra.so does not export {name}"
     assert set(names) == set(B.EXPORTS)
-    assert lib.ra_abi_version() == 1
+    assert lib.ra_abi_version() == 2
 
 
 def test_mask_offset_is_floor_division(lib):
@@ -162,13 +162,16 @@ def test_ring_workspace_and_validation(lib):
     d = _ring_desc()
     assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
     rows = 32 * 32768
-    # one accumulator + one partial: (4 d + 8) bytes per row each
+    # fused schedule: one running state (fp32 O, m, l) per computed position
+    assert n.value == rows * 128 * 4 + 2 * rows * 4
+    s = _ring_desc(separate_merge=1)  # plus one partial per stream
+    assert lib.ra_ring_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.RA_OK
     assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4)
     e = _ring_desc(emulate_copy=1)
     assert lib.ra_ring_workspace_size(ctypes.byref(e), ctypes.byref(n)) == B.RA_OK
-    assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2)
+    assert n.value == (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2)
     for kw in ({"first_pos": 32}, {"n_run": 2}, {"layout": 3}, {"n_pos": 0}, {"block_len": 0},
-               {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}):
+               {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}, {"separate_merge": 2}):
         bad = _ring_desc(**kw)
         assert lib.ra_ring_workspace_size(ctypes.byref(bad), ctypes.byref(n)) != B.RA_OK
     order = (ctypes.c_int32 * 32)(*([0] * 32))

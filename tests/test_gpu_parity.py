@@ -191,7 +191,7 @@ def test_config2_noncausal_bf16_all_rows():
     qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
     qs, ks, vs = (gh.shards_on_device(x, N, "contiguous", "bf16") for x in (qn, kn, vn))
     o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", False, stats=True)
-    assert st["block_launches"] == 4 and st["merge_launches"] == 2 and st["blocks_skipped"] == 0
+    assert st["block_launches"] == 4 and st["merge_launches"] == 2 and st["blocks_skipped"] == 0  # 1 finalise each
     assert st["flops"] == 4 * D * H * S * S
     hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
     gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "contiguous", 0, False, "bf16")
@@ -295,3 +295,64 @@ def test_brute_force_causal_grid(dtype, lay):
         o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
         hh, tt = np.meshgrid(np.arange(2), np.arange(S), indexing="ij")
         gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, True, dtype)
+
+
+# ------------------------------------------------------------------ fused merge
+@pytest.mark.parametrize("dtype,D,flags", [("bf16", 128, 0), ("bf16", 64, 0), ("f32", 40, 0), ("bf16", 128, 1)])
+def test_block_accumulate_equals_separate_merge(dtype, D, flags):
+    """RA_BLOCK_ACCUMULATE merges a block into a running state exactly like
+    computing the partial and folding it in with ra_lse_merge."""
+    B, H, q_len, kv_len, split = 1, 3, 300, 333, 150
+    gh.say("ra_block_attn_fwd accumulate", dtype, D, flags)
+    qn = ra_inputs.normal((B, H, q_len, D), 0, seed=6, dtype=dtype)
+    kn = ra_inputs.normal((B, H, kv_len, D), 1, seed=6, dtype=dtype)
+    vn = ra_inputs.normal((B, H, kv_len, D), 2, seed=6, dtype=dtype)
+    q, k, v = (gh.to_device(x, dtype) for x in (qn, kn, vn))
+    off = 140
+    def part(lo, hi, o, m, l, extra=0):
+        ra.ra_block_attn_fwd(q, k[:, :, lo:hi], v[:, :, lo:hi], o, m, l, causal=True, q_pos0=off, k_pos0=lo,
+                             flags=flags | extra)
+    new = lambda: (torch.empty(B, H, q_len, D, device="cuda"), torch.empty(B, H, q_len, device="cuda"),
+                   torch.empty(B, H, q_len, device="cuda"))
+    acc, pb, ref = new(), new(), new()
+    part(0, split, *acc)
+    part(0, split, *ref)
+    part(split, kv_len, *pb)
+    ra.ra_lse_merge(*ref, *pb)                           # separate: partial + fold
+    part(split, kv_len, *acc, extra=ra.RA_BLOCK_ACCUMULATE)  # fused
+    # an empty running state (m = -inf) is the identity
+    emp = (torch.zeros(B, H, q_len, D, device="cuda"), torch.full((B, H, q_len), float("-inf"), device="cuda"),
+           torch.zeros(B, H, q_len, device="cuda"))
+    part(split, kv_len, *emp, extra=ra.RA_BLOCK_ACCUMULATE)
+    torch.cuda.synchronize()
+    assert torch.equal(acc[1], ref[1])
+    assert torch.allclose(acc[2], ref[2], rtol=2e-6, atol=0)
+    assert torch.allclose(acc[0], ref[0], rtol=2e-6, atol=1e-6)
+    assert torch.equal(emp[1], pb[1]) and torch.allclose(emp[2], pb[2], rtol=1e-6, atol=0)
+    assert torch.allclose(emp[0], pb[0], rtol=1e-6, atol=1e-7)
+    o, m, l = (gh.to_host_f64(x) for x in acc)
+    tol = gh.TOL[dtype]
+    for h in range(H):
+        r = oracle.rows(qn[0, h], kn[0, h], vn[0, h], q_pos=np.arange(q_len) + off, causal=True)
+        assert np.max(np.abs(m[0, h] - r["m"])) <= 1e-4
+        assert np.max(np.abs(o[0, h] / l[0, h][:, None] - r["o"])) <= tol["o"]
+        assert np.max(np.abs(m[0, h] + np.log(l[0, h]) - r["lse"])) <= tol["lse"]
+
+
+@pytest.mark.parametrize("lay,causal", [("striped", True), ("contiguous", True), ("contiguous", False)])
+def test_fused_and_separate_merge_rings_agree(lay, causal):
+    gh.say("ra_ring_forward fused vs separate", lay, causal)
+    N, S, H = 4, 2048, 4
+    (qn, kn, vn), (qs, ks, vs) = _small_ring_inputs(S=S, H=H, N=N, lay=lay)
+    o1, l1, st1 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, stats=True)
+    o2, l2, st2 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, separate_merge=True, stats=True)
+    # fused: one finalising pass per position; separate: one fold per block after the
+    # first (the last one also finalises), and one pass where a position has a single block
+    singles = 1 if (lay == "contiguous" and causal) else 0
+    assert st1["merge_launches"] == N
+    assert st2["merge_launches"] == st2["block_launches"] - N + singles
+    assert torch.max(torch.abs(o1.float() - o2.float())) <= 1e-2
+    assert torch.max(torch.abs(l1 - l2)) <= 1e-5
+    hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    for o, lse in ((o1, l1), (o2, l2)):
+        gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, causal, "bf16")
