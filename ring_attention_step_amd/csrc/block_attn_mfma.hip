@@ -105,11 +105,39 @@ __device__ inline int swz(int r) {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// Maximum with NaN propagation (IEEE 754-2019 maximum).  Unlike fmaxf it needs
+// no quieting of its operands first, and two of them fuse into one
+// three-operand v_maximum3_f32.  Scores are finite or -inf, so the NaN rule
+// never applies.
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum of N values as a tree of three-operand maxima: ceil((N - 1) / 2)
+// instructions, depth ceil(log3 N).
+template <int N>
+__device__ inline float max_tree(const float* x) {
+    if constexpr (N == 1) {
+        return x[0];
+    } else if constexpr (N == 2) {
+        return vmax(x[0], x[1]);
+    } else {
+        constexpr int M = (N + 2) / 3;
+        float y[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const int b = 3 * i;
+            if (b + 2 < N) y[i] = vmax(vmax(x[b], x[b + 1]), x[b + 2]);
+            else if (b + 1 < N) y[i] = vmax(x[b], x[b + 1]);
+            else y[i] = x[b];
+        }
+        return max_tree<M>(y);
+    }
+}
+
 // Combine a lane's value with lane ^ 32's (v_permlane32_swap exchanges halves).
 __device__ inline float xhalf_max(float x) {
     const uint32_t u = __float_as_uint(x);
     auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float xhalf_sum(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -301,18 +329,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
                 }
             }
         }
-        // row max as a balanced tree (short dependency chains)
-        float mt[8 * kSub];
+        // row max: this lane's 16 kSub scores, then the other half-wave's
+        float mt[16 * kSub];
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-            for (int v = 0; v < 8; ++v) mt[8 * sub + v] = fmaxf(sacc[sub][2 * v], sacc[sub][2 * v + 1]);
-#pragma unroll
-        for (int w = 4 * kSub; w >= 1; w >>= 1)
-#pragma unroll
-            for (int v = 0; v < w; ++v) mt[v] = fmaxf(mt[v], mt[v + w]);
-        const float mx = xhalf_max(mt[0]) * c2;
-        m_true = fmaxf(m_true, mx);
+            for (int v = 0; v < 16; ++v) mt[16 * sub + v] = sacc[sub][v];
+        const float mx = xhalf_max(max_tree<16 * kSub>(mt)) * c2;
+        m_true = vmax(m_true, mx);
         const bool move = mx > m_ref + kTau;
         if (__builtin_amdgcn_ballot_w64(move)) {  // rare: re-reference the running state
             const float m_new = move ? mx : m_ref;
