@@ -282,6 +282,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     };
     auto issue_k = [&](int t) __attribute__((always_inline)) { issue_copy(kp, ks2, kcp, t, t & 1); };
     auto issue_v = [&](int t) __attribute__((always_inline)) { issue_copy(vp, vs2, vcp, t, 2 + (t & 1)); };
+    // Ping-pong copies: group 0 copies K tiles, group 1 V tiles, each group's
+    // four waves one instruction at a time from inside their MFMA stream.
+    // Instruction i of wave slot w (w = wave mod WAVES/2) fills chunk
+    // positions [64 (w PER_G + i), +64) of the tile: rows crow0 + RPI i.
+    constexpr int PER_G = INSTR / (WAVES / 2);  // copy instructions per wave per tile
+    constexpr int RPI = 64 / CPR;               // tile rows per copy instruction
+    static_assert(INSTR % (WAVES / 2) == 0, "tile copy must split evenly over a wave group");
+    const int wslot = wave % (WAVES / 2);
+    const int crow0 = wslot * PER_G * RPI + lane / CPR;
+    uint32_t cc16[PER_G];
+#pragma unroll
+    for (int i = 0; i < PER_G; ++i) cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
 
     // per-lane LDS byte offsets of the operand reads
     const lds_char* lds = LDS_PTR(char, smem);
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // that distance, so LDS latency hides behind the MFMAs in flight.
     constexpr int kPf = RA_MFMA_PREFETCH;
     constexpr int NPV = 2 * kSub * (D / 32), NQK = kSub * (D / 16), NT = NPV + NQK;
-    auto mfma_stream = [&]<bool PV, bool QK>(int tp, int tq) __attribute__((always_inline)) {
+    auto mfma_stream = [&]<bool PV, bool QK>(int tp, int tq, auto&& hook) __attribute__((always_inline)) {
         constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NT : NPV, N = I1 - I0;
         const lds_char* vst = lds + (2 + (tp & 1)) * TILE_BYTES;
         const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
@@ -408,9 +420,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
             const bf16x8 op = ops[n % kPf];
             if (n + kPf < N) ops[n % kPf] = load_op(I0 + n + kPf);
             run_mfma(I0 + n, op);
+            hook(n);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    auto no_hook = [](int) __attribute__((always_inline)) {};
 
 #if RA_MFMA_PINGPONG
     // Two groups of WAVES/2 waves (one wave per SIMD each), half a tile apart.
@@ -427,9 +441,35 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // below before any copy), so the PV product adds exactly zero, and scores
     // of an unseen tile are never read.  A group's phase lasts as long as its
     // slowest wave, so skipping would not shorten it.
+    // Copies.  Group 0's MFMA half of tile t (global phase 2t) copies K(t+1);
+    // group 1's (phase 2t+1) copies V(t).  Both buffers' last readers
+    // finished in phase 2t-1, both tiles are awaited at the end of phase
+    // 2t+1, and neither is read before phase 2t+2.  Each wave issues its
+    // PER_G instructions one every kStep MFMA steps over the first half of its
+    // stream, so no wave stalls on a full memory-request queue.  Everything
+    // group-dependent is wave-uniform and selected, not branched on, so both
+    // groups run one MFMA stream.  A tile index past the block copies the last
+    // tile instead (into a buffer no one reads any more; awaited like the
+    // others), and rows past the block re-read its last row.
+    constexpr int kStep = (NT / 2) / PER_G;
+    static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
     auto mfma_half = [&](int t) __attribute__((always_inline)) {
+        const bool gk = group == 0;
+        const int tt = gk ? t + 1 : t;
+        const int tc = min(tt, n_tiles - 1);
+        const int64_t stride = gk ? ks2 : vs2;
+        const uint16_t* src = (gk ? kp : vp) + static_cast<int64_t>(tc) * kNk * stride;
+        const uint32_t stride2 = static_cast<uint32_t>(stride * 2);
+        const int last = a.kv_len - 1 - tc * kNk;  // last row of the block within tile tc
+        const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
         if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        mfma_stream.template operator()<true, true>(t - 1, t);
+        mfma_stream.template operator()<true, true>(t - 1, t, [&](int n) __attribute__((always_inline)) {
+            if (n % kStep == 0 && n / kStep < PER_G) {
+                const int i = n / kStep;
+                const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
+                lds_dma16(src, o, dst + i * 1024);
+            }
+        });
         if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
     };
     auto valu_half = [&](int t) __attribute__((always_inline)) {
@@ -456,23 +496,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         issue_k(0);
         wait_vmem_all();
         __syncthreads();
-        if (group == 1) {
-            if (1 < n_tiles) issue_k(1);
-            issue_v(0);
-            __syncthreads();
-        }
+        if (group == 1) __syncthreads();
         for (int t = 0; t <= n_tiles; ++t) {
-            if (group == 0) {
-                if (t + 1 < n_tiles) issue_k(t + 1);
-                if (t < n_tiles) issue_v(t);
-            }
             mfma_half(t);
             if (group == 1) wait_vmem_all();
             __syncthreads();
-            if (group == 1) {
-                if (t + 2 < n_tiles) issue_k(t + 2);
-                if (t + 1 < n_tiles) issue_v(t + 1);
-            }
             valu_half(t);
             if (group == 0) wait_vmem_all();
             __syncthreads();
@@ -492,9 +520,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
             issue_v(t + 1);
         }
         if (!visible(t)) continue;  // nothing visible to this wave here
-        mfma_stream.template operator()<false, true>(t, t);
+        mfma_stream.template operator()<false, true>(t, t, no_hook);
         softmax(t);
-        mfma_stream.template operator()<true, false>(t, t);
+        mfma_stream.template operator()<true, false>(t, t, no_hook);
     }
 #endif
 
