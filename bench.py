@@ -69,10 +69,28 @@ def traffic_from_profile(kernel_src):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2):
+def _openmp():
+    """The OpenMP runtime the oracle library runs on (to pin its thread count)."""
+    import ctypes
+
+    try:
+        return ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+
+
+def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2, threads=None):
     """Time the oracle on seeded query rows of the workload, in chunks of 32 rows,
-    until about budget_s seconds of CPU work have been done."""
+    until about budget_s seconds of CPU work have been done.  threads=None uses
+    every host core the process may run on."""
     import oracle
+
+    gomp = _openmp()
+    avail = len(os.sched_getaffinity(0))
+    if threads is None:
+        threads = min(int(os.environ.get("OMP_NUM_THREADS", "0")) or avail, avail)
+    if gomp is not None:
+        gomp.omp_set_num_threads(threads)
 
     rng = np.random.Generator(np.random.PCG64(seed))
     S, N, Hq, Hkv = cfg["S"], cfg["N"], cfg["Hq"], cfg["Hkv"]
@@ -93,8 +111,6 @@ def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2):
         dt += time.perf_counter() - t0
         pairs += int(np.sum(t + 1)) if cfg["causal"] else len(t) * S
         rows += len(t)
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    threads = min(threads, len(os.sched_getaffinity(0)))
     flops = 4.0 * cfg["D"] * pairs
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows} seeded query rows of this workload (one head per 32-row chunk), each over its "
@@ -104,8 +120,8 @@ def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
@@ -171,14 +187,14 @@ def main():
                         separate_merge=args.separate_merge)
     workspace = torch.empty(ra.ra_ring_workspace_size(desc), dtype=torch.uint8, device=dev)
 
-    def step(stats):
+    def step(stats, n_streams=0):
         ra.ra_stripe_permute(k_g, k_sh, layout=lay, inverse=False, n_pos=N)
         ra.ra_stripe_permute(v_g, v_sh, layout=lay, inverse=False, n_pos=N)
         if q_g is not None:
             ra.ra_stripe_permute(q_g, q_sh, layout=lay, inverse=False, n_pos=N)
         st = ra.ra_ring_forward(q_sh, k_sh, v_sh, o_sh, lse, n_pos=N, first_pos=first, layout=lay,
                                 causal=cfg["causal"], workspace=workspace, stats=stats,
-                                separate_merge=args.separate_merge)
+                                separate_merge=args.separate_merge, n_streams=n_streams)
         if o_full is not None:
             ra.ra_stripe_permute(o_sh, o_full, layout=lay, inverse=True, n_pos=N)
         return st
@@ -189,9 +205,13 @@ def main():
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
     totals = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
+    step_ms = []
     t_start = time.perf_counter()
     for _ in range(args.steps):
+        t_step = time.perf_counter()
         st = step(True)
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - t_step) * 1e3)
         for key in totals:
             totals[key] += st[key]
     torch.cuda.synchronize()
@@ -201,15 +221,28 @@ def main():
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     log(f"{ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
-    # block-attention kernel roofline: algorithmic FLOPs per launch / mean launch time
-    per_launch_flops = totals["flops"] / max(1, totals["block_launches"])
-    per_launch_ms = totals["block_ms"] / max(1, totals["block_launches"])
+    # block-attention kernel roofline: algorithmic FLOPs per launch / mean launch
+    # time.  A full ring runs its positions on several streams, where launches
+    # overlap and event spans overstate each one; its launches are then timed
+    # in a few extra steps on one stream, after the timed region.
+    rt = totals
+    if n_run > 1:
+        rt = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
+        for _ in range(3):
+            st = step(True, n_streams=1)
+            for key in rt:
+                rt[key] += st[key]
+        torch.cuda.synchronize()
+    per_launch_flops = rt["flops"] / max(1, rt["block_launches"])
+    per_launch_ms = rt["block_ms"] / max(1, rt["block_launches"])
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",
-                "launches": totals["block_launches"], "mean_launch_ms": round(per_launch_ms, 4)}
+                "launches": rt["block_launches"], "mean_launch_ms": round(per_launch_ms, 4),
+                "timing": "HIP events around each launch on its stream" +
+                          (" (3 extra steps on one stream)" if n_run > 1 else "")}
 
     # merge kernel: algorithmic bytes per step.  Fused schedule (default): the
     # block kernel folds each partial into the running state, and the merge
@@ -227,24 +260,30 @@ def main():
             merge_bytes += rows_pos * (4 * D + 8 + 2 * D + 4)
         else:
             merge_bytes += (c - 2) * rows_pos * (12 * D + 24) + rows_pos * (8 * D + 16 + 2 * D + 4)
-    n_merge = totals["merge_launches"]
+    n_merge = rt["merge_launches"]
     merge = None
     if n_merge:
-        gbps = merge_bytes * args.steps / (totals["merge_ms"] * 1e-3) / 1e9
+        n_steps = 3 if n_run > 1 else args.steps
+        gbps = merge_bytes * n_steps / (rt["merge_ms"] * 1e-3) / 1e9
         merge = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                  "frac": round(gbps / PEAK_HBM_GBPS, 4), "launches": n_merge,
-                 "mean_launch_ms": round(totals["merge_ms"] / n_merge, 4),
+                 "mean_launch_ms": round(rt["merge_ms"] / n_merge, 4),
                  "bytes_per_step": merge_bytes}
 
     cpu = None
     if args.cpu_seconds > 0:
-        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s")
+        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s on all cores, then a third of that on one")
         cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds)
+        one = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds / 3, threads=1)
+        cpu["one_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
+        # the oracle over one whole step of this workload, at the measured rate (extrapolated)
+        cpu["extrapolated_step_s"] = round(flops_per_step / (cpu["value"] * 1e12), 1)
 
     line = {
         "metric": "ring-attention fwd TFLOP/s (causal-adjusted) + % of MI355X bf16 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
