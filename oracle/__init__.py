@@ -7,7 +7,14 @@ leg may import this package.  It shares no code with the GPU path
 * ``rows``       -- the C routine ``ra_oracle_rows`` (attention_oracle.c): full
                     softmax attention of given query rows over a key set, fp64,
                     plus the (M, Z, numerator) partial of that key set.
+* ``grads``      -- the C routine ``ra_oracle_grads``: dQ, dK, dV of that
+                    attention for an upstream gradient dO (the backward pass the
+                    pages run: "Context Parallelism", "Practical use and
+                    trade-offs"), and one key block's share of them given the
+                    rows' full-key-set lse and D = dO . O.
 * ``attention``  -- [B, H, S, d] wrapper with the grouped-query head mapping.
+* ``attention_grads`` -- [B, H, S, d] gradients, dK and dV summed over the
+                    query heads that share a key/value head.
 * ``ring_steps`` -- the ring loop of the pages, in fp64 numpy (self-tests only).
 * ``layout``     -- contiguous / striped token maps, written as plain loops.
 
@@ -60,6 +67,12 @@ def load(path: str | None = None):
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    g = lib.ra_oracle_grads
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_int64, ctypes.c_double, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     if path is None:
         _lib = lib
     return lib
@@ -148,3 +161,63 @@ def attention(q, k, v, causal=False, scale=None, sel_b=None, sel_h=None, sel_t=N
                      scale=scale, lib=lib)
             o[idx], lse[idx] = r["o"], r["lse"]
     return o, lse
+
+
+def grads(q, k, v, dout, q_pos=None, k_pos=None, causal=False, scale=None, lse=None, delta=None,
+          lib=None):
+    """Gradients of one head's attention of query rows q [n, d] over keys k, v [n_keys, d]
+    for the upstream gradient dout [n, d] (dtype of q).
+
+    lse / delta (fp64 [n], optional): the rows' log-sum-exp and D = dO . O over
+    their full key set; given, the result is this key set's share of the
+    gradients.  Returns a dict of fp64 arrays dq [n, d], dk, dv [n_keys, d],
+    lse [n], delta [n].
+    """
+    q, k, v, dout = (np.ascontiguousarray(x) for x in (q, k, v, dout))
+    code = _dtype_code(q)
+    if any(_dtype_code(x) != code for x in (k, v, dout)):
+        raise TypeError("q, k, v, dout must share a dtype")
+    n, d = q.shape
+    nk = k.shape[0]
+    if k.shape != (nk, d) or v.shape != (nk, d) or dout.shape != (n, d):
+        raise ValueError("shapes: q, dout [n, d]; k, v [n_keys, d]")
+    qp = None if q_pos is None else np.ascontiguousarray(q_pos, dtype=np.int64)
+    kp = None if k_pos is None else np.ascontiguousarray(k_pos, dtype=np.int64)
+    if causal and qp is None:
+        raise ValueError("causal attention needs query positions")
+    li = None if lse is None else np.ascontiguousarray(lse, dtype=np.float64)
+    di = None if delta is None else np.ascontiguousarray(delta, dtype=np.float64)
+    out = {"dq": np.empty((n, d)), "dk": np.empty((nk, d)), "dv": np.empty((nk, d)),
+           "lse": np.empty(n), "delta": np.empty(n)}
+    rc = (lib or load()).ra_oracle_grads(
+        d, float(scale) if scale else 0.0, int(bool(causal)), code, n, _ptr(q), _ptr(qp), _ptr(dout),
+        nk, _ptr(k), _ptr(v), _ptr(kp), _ptr(li), _ptr(di), _ptr(out["dq"]), _ptr(out["dk"]),
+        _ptr(out["dv"]), _ptr(out["lse"]), _ptr(out["delta"]))
+    if rc != 0:
+        raise RuntimeError(f"ra_oracle_grads failed ({rc})")
+    return out
+
+
+def attention_grads(q, k, v, dout, causal=False, scale=None, lib=None):
+    """dQ [B, Hq, S, d], dK, dV [B, Hkv, S, d] of full attention (global token order).
+
+    Query head h reads key/value head h // (Hq // Hkv); a key/value head's
+    gradients are the sum over the query heads that read it.
+    """
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("q heads must be a multiple of kv heads")
+    g = Hq // Hkv
+    dq = np.empty((B, Hq, S, d))
+    dk = np.zeros((B, Hkv, S, d))
+    dv = np.zeros((B, Hkv, S, d))
+    pos = np.arange(S, dtype=np.int64)
+    for b in range(B):
+        for h in range(Hq):
+            r = grads(q[b, h], k[b, h // g], v[b, h // g], dout[b, h], q_pos=pos, causal=causal,
+                      scale=scale, lib=lib)
+            dq[b, h] = r["dq"]
+            dk[b, h // g] += r["dk"]
+            dv[b, h // g] += r["dv"]
+    return dq, dk, dv

@@ -113,3 +113,185 @@ int ra_oracle_rows(int64_t d, double scale, int causal, int dtype, int64_t n_row
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Gradients of the same attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * The pages run the backward pass: "Context Parallelism" (Ultralytics
+ * glossary), section "Practical use and trade-offs", marks q, k, v as
+ * requiring gradients and back-propagates a loss through the causal attention
+ * output.  For O = softmax(S) V with S = sigma Q K^T (masked entries excluded)
+ * and an upstream gradient dO = dL/dO, the chain rule gives, per query row t
+ * and allowed key c:
+ *     p_tc   = exp(s_tc - lse_t)                     (the softmax weights)
+ *     dp_tc  = dO_t . v_c                            (dL/dp_tc)
+ *     D_t    = sum_{c in C_t} p_tc dp_tc             (= dO_t . O_t)
+ *     ds_tc  = p_tc (dp_tc - D_t)                    (dL/ds_tc, softmax Jacobian)
+ *     dQ_t   = sigma sum_{c in C_t} ds_tc k_c
+ *     dK_c   = sigma sum_{t : c in C_t} ds_tc q_t
+ *     dV_c   = sum_{t : c in C_t} p_tc dO_t
+ * Pass 1 runs over query rows (lse_t, D_t, dQ_t), pass 2 over keys (dK_c,
+ * dV_c) with the lse_t and D_t of pass 1; both evaluate the definitions above
+ * directly in fp64.
+ *
+ * lse_in / delta_in (fp64 [n_rows], may be NULL): use these lse_t and D_t
+ * instead of computing them over the given keys -- this gives one key block's
+ * share of the gradients when lse and D belong to the row's full key set.
+ * dout has the dtype of q, k, v.  dq [n_rows, d], dk, dv [n_keys, d],
+ * lse_out, delta_out [n_rows]: any may be NULL.  Returns 0, -1 on bad
+ * arguments, -2 if scratch memory could not be allocated.
+ */
+int ra_oracle_grads(int64_t d, double scale, int causal, int dtype, int64_t n_rows,
+                    const void* q, const int64_t* q_pos, const void* dout, int64_t n_keys,
+                    const void* k, const void* v, const int64_t* k_pos, const double* lse_in,
+                    const double* delta_in, double* dq, double* dk, double* dv, double* lse_out,
+                    double* delta_out) {
+    if (d <= 0 || n_rows < 0 || n_keys < 0 || (n_rows > 0 && (!q || !dout)) ||
+        (n_keys > 0 && (!k || !v)))
+        return -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+    if (causal && !q_pos) return -1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    double* lse = (double*)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1));
+    double* delta = (double*)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1));
+    if (!lse || !delta) {
+        free(lse);
+        free(delta);
+        return -2;
+    }
+    int failed = 0;
+
+    /* pass 1: per query row */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
+        double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+        double* gr = (double*)malloc(sizeof(double) * (size_t)d);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+        if (!s || !qr || !gr || !acc) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (!s || !qr || !gr || !acc) continue;
+            for (int64_t j = 0; j < d; ++j) {
+                qr[j] = load_elem(q, dtype, r * d + j);
+                gr[j] = load_elem(dout, dtype, r * d + j);
+            }
+            double M = -INFINITY;
+            for (int64_t c = 0; c < n_keys; ++c) {
+                const int64_t pc = k_pos ? k_pos[c] : c;
+                if (causal && pc > q_pos[r]) continue;
+                double dot = 0.0;
+                for (int64_t j = 0; j < d; ++j) dot += qr[j] * load_elem(k, dtype, c * d + j);
+                s[c] = scale * dot;
+                if (s[c] > M) M = s[c];
+            }
+            double L;
+            if (lse_in) {
+                L = lse_in[r];
+            } else if (M == -INFINITY) {
+                L = -INFINITY;
+            } else {
+                double Z = 0.0;
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    const int64_t pc = k_pos ? k_pos[c] : c;
+                    if (causal && pc > q_pos[r]) continue;
+                    Z += exp(s[c] - M);
+                }
+                L = M + log(Z);
+            }
+            /* D_t = sum p dp (or given) */
+            double D = 0.0;
+            if (delta_in) {
+                D = delta_in[r];
+            } else if (L != -INFINITY) {
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    const int64_t pc = k_pos ? k_pos[c] : c;
+                    if (causal && pc > q_pos[r]) continue;
+                    double dp = 0.0;
+                    for (int64_t j = 0; j < d; ++j) dp += gr[j] * load_elem(v, dtype, c * d + j);
+                    D += exp(s[c] - L) * dp;
+                }
+            }
+            /* dQ_t = sigma sum ds k */
+            for (int64_t j = 0; j < d; ++j) acc[j] = 0.0;
+            if (L != -INFINITY) {
+                for (int64_t c = 0; c < n_keys; ++c) {
+                    const int64_t pc = k_pos ? k_pos[c] : c;
+                    if (causal && pc > q_pos[r]) continue;
+                    double dp = 0.0;
+                    for (int64_t j = 0; j < d; ++j) dp += gr[j] * load_elem(v, dtype, c * d + j);
+                    const double p = exp(s[c] - L);
+                    const double ds = p * (dp - D);
+                    for (int64_t j = 0; j < d; ++j) acc[j] += ds * load_elem(k, dtype, c * d + j);
+                }
+            }
+            if (dq)
+                for (int64_t j = 0; j < d; ++j) dq[r * d + j] = scale * acc[j];
+            lse[r] = L;
+            delta[r] = D;
+        }
+        free(s);
+        free(qr);
+        free(gr);
+        free(acc);
+    }
+
+    /* pass 2: per key */
+    if (!failed && (dk || dv)) {
+#pragma omp parallel
+        {
+            double* kr = (double*)malloc(sizeof(double) * (size_t)d);
+            double* vr = (double*)malloc(sizeof(double) * (size_t)d);
+            double* ak = (double*)malloc(sizeof(double) * (size_t)d);
+            double* av = (double*)malloc(sizeof(double) * (size_t)d);
+            if (!kr || !vr || !ak || !av) {
+#pragma omp atomic write
+                failed = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t c = 0; c < n_keys; ++c) {
+                if (!kr || !vr || !ak || !av) continue;
+                const int64_t pc = k_pos ? k_pos[c] : c;
+                for (int64_t j = 0; j < d; ++j) {
+                    kr[j] = load_elem(k, dtype, c * d + j);
+                    vr[j] = load_elem(v, dtype, c * d + j);
+                    ak[j] = 0.0;
+                    av[j] = 0.0;
+                }
+                for (int64_t r = 0; r < n_rows; ++r) {
+                    if (causal && pc > q_pos[r]) continue;
+                    if (lse[r] == -INFINITY) continue;
+                    double dot = 0.0, dp = 0.0;
+                    for (int64_t j = 0; j < d; ++j) {
+                        dot += load_elem(q, dtype, r * d + j) * kr[j];
+                        dp += load_elem(dout, dtype, r * d + j) * vr[j];
+                    }
+                    const double p = exp(scale * dot - lse[r]);
+                    const double ds = p * (dp - delta[r]);
+                    for (int64_t j = 0; j < d; ++j) {
+                        av[j] += p * load_elem(dout, dtype, r * d + j);
+                        ak[j] += ds * load_elem(q, dtype, r * d + j);
+                    }
+                }
+                for (int64_t j = 0; j < d; ++j) {
+                    if (dk) dk[c * d + j] = scale * ak[j];
+                    if (dv) dv[c * d + j] = av[j];
+                }
+            }
+            free(kr);
+            free(vr);
+            free(ak);
+            free(av);
+        }
+    }
+    if (lse_out)
+        for (int64_t r = 0; r < n_rows; ++r) lse_out[r] = lse[r];
+    if (delta_out)
+        for (int64_t r = 0; r < n_rows; ++r) delta_out[r] = delta[r];
+    free(lse);
+    free(delta);
+    return failed ? -2 : 0;
+}
