@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 2
+#define RA_ABI_VERSION 3
 
 typedef enum ra_status {
     RA_OK = 0,
@@ -154,7 +154,8 @@ typedef struct ra_ring_stats {
     int64_t block_launches, merge_launches, copy_launches;
     int64_t blocks_skipped;             /* (position, step) pairs fully masked, skipped */
     double unmasked_pairs;              /* (query row, key) pairs attended, all heads   */
-    double flops;                       /* 4 * head_dim * unmasked_pairs                */
+    double flops;                       /* ra_ring_forward: 4 * head_dim * unmasked_pairs;
+                                           ra_ring_backward: 10 * head_dim * unmasked_pairs */
 } ra_ring_stats;
 
 /*
@@ -237,6 +238,68 @@ ra_status ra_ring_forward(const ra_ring_desc* desc, const void* q, const void* k
 ra_status ra_stripe_permute(int32_t layout, int32_t inverse, int32_t dtype, int32_t batch,
                             int32_t heads, int64_t seq_len, int32_t head_dim, int32_t n_pos,
                             const void* x, void* y, void* stream);
+
+/*
+ * Backward pass.  The pages run it: "Context Parallelism" (Ultralytics
+ * glossary), section "Practical use and trade-offs", marks q, k, v as
+ * requiring gradients and back-propagates a loss through the causal
+ * attention.  For an upstream gradient dO = dL/dO, with p_rc the forward's
+ * softmax weights exp(s_rc - lse_r) and delta_r = dO_r . O_r, the chain rule
+ * gives  dp_rc = dO_r . v_c,  ds_rc = p_rc (dp_rc - delta_r),
+ *   dQ_r = scale sum_c ds_rc k_c,  dK_c = scale sum_r ds_rc q_r,
+ *   dV_c = sum_r p_rc dO_r   (sums over visible pairs).
+ * Summed over key blocks these give the full gradients, so a ring adds each
+ * step's share: dQ stays with its position, dK and dV travel with their block.
+ */
+
+/* ra_attn_bwd_delta -- delta[r] = sum_j dout[r, j] * o[r, j] (binary32) for
+ * rows x head_dim arrays o, dout in dtype (dense, row-major).  o is the
+ * forward's normalised output. */
+ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const void* o,
+                            const void* dout, float* delta, void* stream);
+
+/*
+ * ra_block_attn_bwd -- one query block against one key/value block: ADDS this
+ * block pair's share of the gradients into dq, dk, dv.
+ *
+ * desc, q, k, v: as for ra_block_attn_fwd (flags: only RA_BLOCK_FORCE_SIMT).
+ * dout: [batch, q_heads, q_len, head_dim] in dtype at q's strides.
+ * lse, delta: [batch, q_heads, q_len] binary32, dense: the rows' log-sum-exp
+ *   over their FULL key set (ra_ring_forward's lse) and ra_attn_bwd_delta.
+ *   Rows with lse = -inf contribute nothing.
+ * dq: [batch, q_heads, q_len, head_dim]; dk, dv: [batch, kv_heads, kv_len,
+ *   head_dim]; binary32, dense, accumulated into (+=).  A key/value head's
+ *   dk, dv sum over the query heads that read it; no atomics are used, so
+ *   concurrent calls must not share an output array.
+ * q_len == 0 or kv_len == 0 is a no-op.
+ */
+ra_status ra_block_attn_bwd(const ra_block_desc* desc, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse,
+                            const float* delta, float* dq, float* dk, float* dv, void* stream);
+
+/* Bytes of device workspace ra_ring_backward needs (256-byte aligned base). */
+ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* desc, size_t* bytes);
+
+/*
+ * ra_ring_backward -- the ring backward for N virtual positions on one GPU.
+ * Steps run in lockstep as on a real ring: at step s position i holds block
+ * j = (i - visit_order[s]) mod n_pos (distinct across positions) and adds its
+ * share into its own dq and into the block's dk, dv.  Fully masked pairs are
+ * skipped.  All work runs on `stream`; emulate_copy, n_streams and
+ * separate_merge are ignored.  With desc->stats, backward launches are timed
+ * (block_ms, block_launches) and flops counts the five products.
+ *
+ * q, o, dout: [n_run, batch, q_heads, Sb, head_dim] in dtype (o and lse from
+ *   ra_ring_forward on the same desc);  lse: [n_run, batch, q_heads, Sb];
+ * k, v: [n_pos, batch, kv_heads, Sb, head_dim] in dtype;
+ * dq: [n_run, batch, q_heads, Sb, head_dim] binary32 (overwritten);
+ * dk, dv: [n_pos, batch, kv_heads, Sb, head_dim] binary32 (overwritten with
+ *   the run positions' share: the full gradients when n_run == n_pos).
+ */
+ra_status ra_ring_backward(const ra_ring_desc* desc, const void* q, const void* k,
+                           const void* v, const void* o, const void* dout, const float* lse,
+                           float* dq, float* dk, float* dv, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Host-side helpers (no GPU work; usable on a machine without a GPU). */
 

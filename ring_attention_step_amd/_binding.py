@@ -58,7 +58,8 @@ class ra_ring_desc(ctypes.Structure):
 
 EXPORTS = ["ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_forward",
            "ra_stripe_permute", "ra_mask_offset", "ra_unmasked_pairs", "ra_ring_pair_offset",
-           "ra_last_error", "ra_abi_version", "ra_release"]
+           "ra_last_error", "ra_abi_version", "ra_release", "ra_attn_bwd_delta", "ra_block_attn_bwd",
+           "ra_ring_bwd_workspace_size", "ra_ring_backward"]
 
 _lib = None
 
@@ -95,6 +96,15 @@ def load_library(path: str = LIB_PATH):
     lib.ra_abi_version.restype = i32
     lib.ra_release.argtypes = []
     lib.ra_release.restype = None
+    lib.ra_attn_bwd_delta.argtypes = [i64, i32, i32, vp, vp, vp, vp]
+    lib.ra_attn_bwd_delta.restype = ctypes.c_int
+    lib.ra_block_attn_bwd.argtypes = [ctypes.POINTER(ra_block_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ra_block_attn_bwd.restype = ctypes.c_int
+    lib.ra_ring_bwd_workspace_size.argtypes = [ctypes.POINTER(ra_ring_desc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ra_ring_bwd_workspace_size.restype = ctypes.c_int
+    lib.ra_ring_backward.argtypes = [ctypes.POINTER(ra_ring_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
+    lib.ra_ring_backward.restype = ctypes.c_int
     del f32
     if path == LIB_PATH:
         _lib = lib
@@ -285,3 +295,67 @@ def ra_stripe_permute(x, y, *, layout, inverse, n_pos, stream=None):
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     _check(load_library().ra_stripe_permute(lay, int(bool(inverse)), _dtype(x), B, H, S, D, N, _ptr(x), _ptr(y),
                                             _stream(stream)))
+
+
+# ------------------------------------------------------------------ backward
+def ra_attn_bwd_delta(o, dout, delta, stream=None):
+    """delta [rows] = sum over head_dim of dout * o (o, dout [..., D] dense, same dtype)."""
+    _need_dense(o, "o")
+    _need_dense(dout, "dout", o.dtype)
+    _need_dense(delta, "delta", torch.float32)
+    D = o.shape[-1]
+    rows = o.numel() // D if D else 0
+    if dout.shape != o.shape or delta.numel() != rows:
+        raise ValueError("dout must match o; delta needs one value per row")
+    _check(load_library().ra_attn_bwd_delta(rows, D, _dtype(o), _ptr(o), _ptr(dout), _ptr(delta),
+                                            _stream(stream)))
+
+
+def ra_block_attn_bwd(q, k, v, dout, lse, delta, dq, dk, dv, *, causal=False, scale=0.0, q_pos0=0, k_pos0=0,
+                      pos_stride=1, flags=0, stream=None):
+    """Add one block pair's share of dQ [B,Hq,q_len,D], dK, dV [B,Hkv,kv_len,D] (fp32)."""
+    if dout.shape != q.shape or dout.dtype != q.dtype or tuple(dout.stride()) != tuple(q.stride()):
+        raise ValueError("dout must have q's shape, dtype and strides")
+    for t, name in ((lse, "lse"), (delta, "delta"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need_dense(t, name, torch.float32)
+    if tuple(dq.shape) != tuple(q.shape) or tuple(dk.shape) != tuple(k.shape) or dv.shape != dk.shape:
+        raise ValueError("dq must be shaped like q, dk and dv like k")
+    if tuple(lse.shape) != tuple(q.shape[:3]) or lse.shape != delta.shape:
+        raise ValueError("lse and delta must be shaped like q without head_dim")
+    d = block_desc(q, k, v, causal, scale, q_pos0, k_pos0, pos_stride, flags)
+    _check(load_library().ra_block_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
+                                            _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def ra_ring_bwd_workspace_size(desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().ra_ring_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ra_ring_backward(q, k, v, o, dout, lse, dq, dk, dv, *, n_pos, first_pos=0, layout="contiguous",
+                     causal=False, scale=0.0, visit_order=None, workspace=None, stats=False, stream=None):
+    """Gradients of the ring: dq [n_run,B,Hq,Sb,D], dk, dv [n_pos,B,Hkv,Sb,D] (fp32, overwritten).
+
+    Returns a dict of ra_ring_stats when stats=True, else None.
+    """
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need_dense(t, name)
+    for t, name in ((lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need_dense(t, name, torch.float32)
+    if v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("v must match k; o, dout, dq must match q")
+    if dk.shape != k.shape or dv.shape != k.shape or tuple(lse.shape) != tuple(q.shape[:4]):
+        raise ValueError("dk, dv must match k; lse must be q's shape without head_dim")
+    st = ra_ring_stats() if stats else None
+    d = ring_desc(q, k, n_pos=n_pos, first_pos=first_pos, layout=layout, causal=causal, scale=scale,
+                  visit_order=visit_order, stats=st)
+    need = ra_ring_bwd_workspace_size(d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(load_library().ra_ring_backward(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)))
+    if st is None:
+        return None
+    return {name: getattr(st, name) for name, _ in ra_ring_stats._fields_}

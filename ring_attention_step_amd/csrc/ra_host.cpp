@@ -588,6 +588,190 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     return RA_OK;
 }
 
+// ------------------------------------------------------------------ backward
+ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const void* o, const void* dout,
+                            float* delta, void* stream) {
+    if (rows < 0) return fail(RA_ERR_INVALID, "rows must be >= 0");
+    if (head_dim < 1) return fail(RA_ERR_INVALID, "head_dim must be >= 1");
+    if (!valid_dtype(dtype)) return fail(RA_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+    if (rows == 0) return RA_OK;
+    if (!o || !dout || !delta) return fail(RA_ERR_INVALID, "null pointer");
+    if (!aligned_to(o, elem_size(dtype)) || !aligned_to(dout, elem_size(dtype)) || !aligned_to(delta, 4))
+        return fail(RA_ERR_INVALID, "misaligned pointer");
+    hipError_t e = ra::launch_bwd_delta(rows, head_dim, dtype, o, dout, delta, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "delta launch");
+    return RA_OK;
+}
+
+ra_status ra_block_attn_bwd(const ra_block_desc* d, const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+    if (!d) return fail(RA_ERR_INVALID, "null descriptor");
+    ra_status st = check_heads(d->batch, d->q_heads, d->kv_heads, d->head_dim, d->dtype);
+    if (st != RA_OK) return st;
+    if (d->q_len < 0 || d->kv_len < 0 || d->q_len > kMaxLen || d->kv_len > kMaxLen)
+        return fail(RA_ERR_INVALID, "q_len / kv_len out of range");
+    if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID, "causal must be 0 or 1");
+    if (d->flags & ~RA_BLOCK_FORCE_SIMT) return fail(RA_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+    if (d->pos_stride < 1) return fail(RA_ERR_INVALID, "pos_stride must be >= 1");
+    if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
+    for (int i = 0; i < 3; ++i)
+        if (d->q_strides[i] < 0 || d->k_strides[i] < 0 || d->v_strides[i] < 0)
+            return fail(RA_ERR_INVALID, "strides must be non-negative");
+    if (d->q_len == 0 || d->kv_len == 0) return RA_OK;
+    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv)
+        return fail(RA_ERR_INVALID, "null pointer");
+    const size_t es = elem_size(d->dtype);
+    if (!aligned_to(q, es) || !aligned_to(k, es) || !aligned_to(v, es) || !aligned_to(dout, es) ||
+        !aligned_to(lse, 4) || !aligned_to(delta, 4) || !aligned_to(dq, 4) || !aligned_to(dk, 4) || !aligned_to(dv, 4))
+        return fail(RA_ERR_INVALID, "misaligned pointer");
+    ra::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.B = d->batch;
+    a.Hq = d->q_heads;
+    a.Hkv = d->kv_heads;
+    a.D = d->head_dim;
+    a.q_len = static_cast<int32_t>(d->q_len);
+    a.kv_len = static_cast<int32_t>(d->kv_len);
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = d->q_strides[i];
+        a.dos[i] = d->q_strides[i];
+        a.ks[i] = d->k_strides[i];
+        a.vs[i] = d->v_strides[i];
+    }
+    a.scale = resolve_scale(d->scale, d->head_dim);
+    a.causal = d->causal;
+    a.mask_offset = clamp_offset(ra_mask_offset(d->q_pos0, d->k_pos0, d->pos_stride), d->q_len, d->kv_len);
+    const hipError_t e = ra::launch_block_bwd(a, d->dtype, d->flags & RA_BLOCK_FORCE_SIMT, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block backward launch");
+    return RA_OK;
+}
+
+ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* d, size_t* bytes) {
+    ra_status st = check_ring(d);
+    if (st != RA_OK) return st;
+    if (!bytes) return fail(RA_ERR_INVALID, "null bytes pointer");
+    const int64_t rows = static_cast<int64_t>(d->batch) * d->q_heads * d->block_len;
+    *bytes = round_up(static_cast<size_t>(d->n_run) * static_cast<size_t>(rows) * 4, 256);
+    return RA_OK;
+}
+
+ra_status ra_ring_backward(const ra_ring_desc* d, const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    ra_status st = check_ring(d);
+    if (st != RA_OK) return st;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return fail(RA_ERR_INVALID, "null pointer");
+    const size_t es = elem_size(d->dtype);
+    if (!aligned_to(q, es) || !aligned_to(k, es) || !aligned_to(v, es) || !aligned_to(o, es) ||
+        !aligned_to(dout, es) || !aligned_to(lse, 4) || !aligned_to(dq, 4) || !aligned_to(dk, 4) || !aligned_to(dv, 4))
+        return fail(RA_ERR_INVALID, "misaligned pointer");
+    size_t need = 0;
+    ra_ring_bwd_workspace_size(d, &need);
+    if (!workspace || workspace_bytes < need)
+        return fail(RA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if (!aligned_to(workspace, 256)) return fail(RA_ERR_INVALID, "workspace must be 256-byte aligned");
+
+    const int32_t N = d->n_pos, D = d->head_dim;
+    const int64_t Sb = d->block_len;
+    const int64_t rows = static_cast<int64_t>(d->batch) * d->q_heads * Sb;
+    const int64_t q_elems = rows * D;
+    const int64_t kv_elems = static_cast<int64_t>(d->batch) * d->kv_heads * Sb * D;
+    const hipStream_t caller = static_cast<hipStream_t>(stream);
+    float* delta = static_cast<float*>(workspace);
+
+    std::vector<std::vector<RingPlanStep>> plan(d->n_run);
+    ra_ring_stats stats{};
+    for (int p = 0; p < d->n_run; ++p) {
+        plan[p] = plan_position(d, d->first_pos + p);
+        for (const auto& ps : plan[p]) {
+            if (ps.skip) ++stats.blocks_skipped;
+            else
+                stats.unmasked_pairs += static_cast<double>(ra_unmasked_pairs(Sb, Sb, d->causal, ps.offset)) *
+                                        d->batch * d->q_heads;
+        }
+    }
+    stats.flops = 10.0 * D * stats.unmasked_pairs;  // five products of 2 d FLOPs per pair
+
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int dev = 0;
+    RA_HIP(hipGetDevice(&dev));
+    DeviceState& ds = g_devices[dev];
+    Timer timer;
+    if (d->stats) timer.pool = &ds.timing_events;
+
+    // gradients start at zero (fill kernels: no memset nodes under graph capture)
+    hipError_t e = ra::launch_fill_zero(dq, static_cast<int64_t>(d->n_run) * q_elems, caller);
+    if (e == hipSuccess) e = ra::launch_fill_zero(dk, static_cast<int64_t>(N) * kv_elems, caller);
+    if (e == hipSuccess) e = ra::launch_fill_zero(dv, static_cast<int64_t>(N) * kv_elems, caller);
+    if (e == hipSuccess) e = ra::launch_bwd_delta(static_cast<int64_t>(d->n_run) * rows, D, d->dtype, o, dout, delta, caller);
+    if (e != hipSuccess) return hip_fail(e, "backward set-up launch");
+
+    // Lockstep over steps, as on a real ring: at step s position i holds block
+    // j = (i - visit[s]) mod N, distinct across positions, and adds its share
+    // into that block's dK, dV (which travel with the block) and into its own
+    // dQ.  All launches go to the caller's stream in that order.
+    for (int32_t s = 0; s < N; ++s) {
+        for (int p = 0; p < d->n_run; ++p) {
+            const RingPlanStep& ps = plan[p][s];
+            if (ps.skip) continue;
+            ra::BwdArgs a{};
+            const char* qb = static_cast<const char*>(q) + static_cast<size_t>(p) * q_elems * es;
+            a.q = qb;
+            a.dout = static_cast<const char*>(dout) + static_cast<size_t>(p) * q_elems * es;
+            a.k = static_cast<const char*>(k) + static_cast<size_t>(ps.block) * kv_elems * es;
+            a.v = static_cast<const char*>(v) + static_cast<size_t>(ps.block) * kv_elems * es;
+            a.lse = lse + p * rows;
+            a.delta = delta + p * rows;
+            a.dq = dq + p * q_elems;
+            a.dk = dk + ps.block * kv_elems;
+            a.dv = dv + ps.block * kv_elems;
+            a.B = d->batch;
+            a.Hq = d->q_heads;
+            a.Hkv = d->kv_heads;
+            a.D = D;
+            a.q_len = static_cast<int32_t>(Sb);
+            a.kv_len = static_cast<int32_t>(Sb);
+            a.qs[0] = static_cast<int64_t>(d->q_heads) * Sb * D;
+            a.qs[1] = Sb * D;
+            a.qs[2] = D;
+            for (int i = 0; i < 3; ++i) a.dos[i] = a.qs[i];
+            a.ks[0] = a.vs[0] = static_cast<int64_t>(d->kv_heads) * Sb * D;
+            a.ks[1] = a.vs[1] = Sb * D;
+            a.ks[2] = a.vs[2] = D;
+            a.scale = resolve_scale(d->scale, D);
+            a.causal = d->causal;
+            a.mask_offset = clamp_offset(ps.offset, Sb, Sb);
+            size_t ti = 0;
+            st = timer.begin(caller, ti);
+            if (st != RA_OK) return st;
+            e = ra::launch_block_bwd(a, d->dtype, 0, caller);
+            if (e != hipSuccess) return hip_fail(e, "block backward launch");
+            st = timer.end(caller, ti, 0);
+            if (st != RA_OK) return st;
+        }
+    }
+    if (d->stats) {
+        RA_HIP(hipStreamSynchronize(caller));
+        for (const auto& sp : timer.spans) {
+            float ms = 0.f;
+            RA_HIP(hipEventElapsedTime(&ms, ds.timing_events[sp.first], ds.timing_events[sp.first + 1]));
+            stats.block_ms += ms;
+            ++stats.block_launches;
+        }
+        *d->stats = stats;
+    }
+    return RA_OK;
+}
+
 void ra_release(void) {
     std::lock_guard<std::mutex> lock(g_mutex);
     int cur = 0;

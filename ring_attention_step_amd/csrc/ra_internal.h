@@ -36,6 +36,40 @@ hipError_t launch_block_simt(const BlockArgs& a, int dtype, hipStream_t s);
 bool mfma_eligible(const BlockArgs& a, int dtype);
 hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s);
 
+// Backward of one query block against one key/value block: this pair's share
+// of the gradients, added into dq [B, Hq, q_len, D] and dk, dv
+// [B, Hkv, kv_len, D] (fp32, contiguous).  lse and delta ([B, Hq, q_len],
+// fp32) belong to the rows' full key set: p = exp(scale s - lse), and
+// delta = dO . O.  dk/dv of a key/value head sum its query heads.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    float* dq;
+    float* dk;
+    float* dv;
+    int32_t B, Hq, Hkv, D;
+    int32_t q_len, kv_len;
+    int64_t qs[3], ks[3], vs[3], dos[3];  // element strides for (b, h, row)
+    float scale;
+    int32_t causal;
+    int32_t mask_offset;  // key c visible to row r iff c <= r + mask_offset
+};
+
+// Vector-ALU backward: binary32 or bfloat16 inputs, any D in [1, 256].
+hipError_t launch_block_bwd_simt(const BwdArgs& a, int dtype, hipStream_t s);
+// Kernel selection for the backward (MFMA where eligible unless force_simt).
+hipError_t launch_block_bwd(const BwdArgs& a, int dtype, int force_simt, hipStream_t s);
+// x[0 .. n) = 0 (fp32), a fill kernel rather than a memset node.
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t s);
+
+// delta[r] = sum_j dout[r, j] * o[r, j] for rows x D (contiguous, dtype), fp32 out.
+hipError_t launch_bwd_delta(int64_t rows, int32_t D, int dtype, const void* o, const void* dout, float* delta,
+                            hipStream_t s);
+
 struct MergeArgs {
     int64_t rows;
     int32_t D;

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     for name in names:
         assert hasattr(lib, name), f"libra.so does not export {name}"
     assert set(names) == set(B.EXPORTS)
-    assert lib.ra_abi_version() == 2
+    assert lib.ra_abi_version() == 3
 
 
 def test_mask_offset_is_floor_division(lib):
@@ -180,4 +180,25 @@ def test_ring_workspace_and_validation(lib):
     assert lib.ra_ring_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.RA_ERR_INVALID
     # too small a workspace is refused before anything runs
     st = lib.ra_ring_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x100000), 1024, None)
+    assert st == B.RA_ERR_WORKSPACE
+
+
+def test_backward_validation(lib):
+    d = _block_desc()
+    args = [FAKE] * 9
+    assert lib.ra_block_attn_bwd(None, *args, None) == B.RA_ERR_INVALID
+    bad = _block_desc(flags=B.RA_BLOCK_ACCUMULATE)  # the backward always accumulates; the flag is not accepted
+    assert lib.ra_block_attn_bwd(ctypes.byref(bad), *args, None) == B.RA_ERR_UNSUPPORTED
+    nulls = [FAKE] * 8 + [None]
+    assert lib.ra_block_attn_bwd(ctypes.byref(d), *nulls, None) == B.RA_ERR_INVALID
+    e = _block_desc(kv_len=0)
+    assert lib.ra_block_attn_bwd(ctypes.byref(e), *([None] * 9), None) == B.RA_OK
+    assert lib.ra_attn_bwd_delta(-1, 64, 0, FAKE, FAKE, FAKE, None) == B.RA_ERR_INVALID
+    assert lib.ra_attn_bwd_delta(4, 64, 9, FAKE, FAKE, FAKE, None) == B.RA_ERR_UNSUPPORTED
+    assert lib.ra_attn_bwd_delta(0, 64, 0, None, None, None, None) == B.RA_OK
+    n = ctypes.c_size_t()
+    r = _ring_desc()
+    assert lib.ra_ring_bwd_workspace_size(ctypes.byref(r), ctypes.byref(n)) == B.RA_OK
+    assert n.value == 32 * 32768 * 4  # one delta per row of the run position
+    st = lib.ra_ring_backward(ctypes.byref(r), *([FAKE] * 9), ctypes.c_void_p(0x100000), 1024, None)
     assert st == B.RA_ERR_WORKSPACE

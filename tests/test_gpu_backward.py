@@ -1,0 +1,160 @@
+"""GPU parity of the backward pass against the fp64 gradient oracle.
+
+Block pairs: ra_block_attn_bwd adds one (query block, key block) share of dQ,
+dK, dV given the rows' full-key-set lse and delta; the oracle computes the
+same share (``oracle.grads`` with lse/delta).  Rings: ra_ring_backward's
+gradients against ``oracle.attention_grads`` in global token order.
+
+Tolerance: max |GPU - oracle| <= tol * max(1, max |oracle|) per tensor, with
+tol = 1e-4 for the fp32-arithmetic kernels (binary32 or bfloat16 inputs
+widened exactly) and 2e-2 where bfloat16 MFMA products round P and dS to
+bfloat16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ra_inputs
+import ring_attention_step_amd as ra
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ra.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _close(got, want, tol, what):
+    err = float(np.max(np.abs(got - want))) if want.size else 0.0
+    ref = max(1.0, float(np.max(np.abs(want)))) if want.size else 1.0
+    assert err <= tol * ref, f"{what}: max |GPU - oracle| = {err:.3e} > {tol} * {ref:.3g}"
+    return err / ref
+
+
+def test_delta_kernel():
+    for dtype, D in (("f32", 48), ("bf16", 128)):
+        gh.say("ra_attn_bwd_delta", dtype, D)
+        o = ra_inputs.normal((1, 3, 257, D), 0, seed=21, dtype=dtype)
+        g = ra_inputs.normal((1, 3, 257, D), 1, seed=21, dtype=dtype)
+        od, gd = gh.to_device(o, dtype), gh.to_device(g, dtype)
+        delta = torch.empty(1, 3, 257, device="cuda")
+        ra.ra_attn_bwd_delta(od, gd, delta)
+        torch.cuda.synchronize()
+        wid = (lambda x: ra_inputs.bf16_to_f32(x)) if dtype == "bf16" else (lambda x: x)
+        want = np.sum(wid(o).astype(np.float64) * wid(g).astype(np.float64), axis=-1)
+        _close(gh.to_host_f64(delta), want, 1e-5, "delta")
+
+
+BLOCK_CASES = [("f32", 16, 1), ("f32", 64, 1), ("f32", 100, 1), ("f32", 256, 1), ("bf16", 64, 1),
+               ("bf16", 128, 1), ("bf16", 128, 0), ("bf16", 64, 0), ("bf16", 48, 0)]
+OFFSETS = [None, 0, -1, 37, -150, 400]
+
+
+@pytest.mark.parametrize("dtype,D,force_simt", BLOCK_CASES)
+def test_block_bwd_matches_oracle(dtype, D, force_simt):
+    B, Hq, Hkv, q_len, kv_len = 1, 4, 2, 300, 333
+    gh.say("ra_block_attn_bwd", dtype, D, force_simt)
+    qn = ra_inputs.normal((B, Hq, q_len, D), 0, seed=31, dtype=dtype)
+    kn = ra_inputs.normal((B, Hkv, kv_len, D), 1, seed=31, dtype=dtype)
+    vn = ra_inputs.normal((B, Hkv, kv_len, D), 2, seed=31, dtype=dtype)
+    gn = ra_inputs.normal((B, Hq, q_len, D), 3, seed=31, dtype=dtype)
+    # q and dout as strided views ([B, S, H, D] memory)
+    q = gh.to_device(np.ascontiguousarray(qn.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+    g = gh.to_device(np.ascontiguousarray(gn.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
+    k, v = gh.to_device(kn, dtype), gh.to_device(vn, dtype)
+    mfma = dtype == "bf16" and D in (64, 128) and not force_simt
+    tol = 2e-2 if mfma else 1e-4
+    grp = Hq // Hkv
+    for off in OFFSETS:
+        causal = off is not None
+        qpos = np.arange(q_len, dtype=np.int64) + (off or 0)
+        # the rows' "full key set" for lse / delta: this block plus keys before it,
+        # so that lse is not this block's own (exercises the share semantics)
+        lse = np.empty((B, Hq, q_len))
+        dlt = np.empty((B, Hq, q_len))
+        want = {"dq": np.zeros((B, Hq, q_len, D)), "dk": np.zeros((B, Hkv, kv_len, D)),
+                "dv": np.zeros((B, Hkv, kv_len, D))}
+        extra = ra_inputs.normal((1, Hkv, 64, D), 1, seed=32, dtype=dtype)
+        for h in range(Hq):
+            kk = np.concatenate([extra[0, h // grp], kn[0, h // grp]])
+            vv = np.concatenate([extra[0, h // grp], vn[0, h // grp]])
+            kpos = np.concatenate([np.arange(-64, 0), np.arange(kv_len)])
+            full = oracle.grads(qn[0, h], kk, vv, gn[0, h], q_pos=qpos, k_pos=kpos, causal=causal)
+            lse[0, h], dlt[0, h] = full["lse"], full["delta"]
+            part = oracle.grads(qn[0, h], kn[0, h // grp], vn[0, h // grp], gn[0, h], q_pos=qpos,
+                                k_pos=np.arange(kv_len), causal=causal, lse=full["lse"], delta=full["delta"])
+            want["dq"][0, h] = part["dq"]
+            want["dk"][0, h // grp] += part["dk"]
+            want["dv"][0, h // grp] += part["dv"]
+        dq = torch.zeros(B, Hq, q_len, D, device="cuda")
+        dk = torch.zeros(B, Hkv, kv_len, D, device="cuda")
+        dv = torch.zeros(B, Hkv, kv_len, D, device="cuda")
+        lse_d = torch.from_numpy(lse.astype(np.float32)).cuda()
+        dlt_d = torch.from_numpy(dlt.astype(np.float32)).cuda()
+        ra.ra_block_attn_bwd(q, k, v, g, lse_d, dlt_d, dq, dk, dv, causal=causal, q_pos0=(off or 0), k_pos0=0,
+                             flags=ra.RA_BLOCK_FORCE_SIMT if force_simt else 0)
+        torch.cuda.synchronize()
+        for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _close(gh.to_host_f64(got), want[name], tol, f"{name} off={off}")
+
+
+def test_block_bwd_accumulates_and_empty_cases():
+    gh.say("ra_block_attn_bwd accumulate / empty")
+    D = 64
+    q = torch.randn(1, 2, 40, D, device="cuda")
+    k = torch.randn(1, 2, 50, D, device="cuda")
+    lse = torch.full((1, 2, 40), 3.0, device="cuda")
+    dlt = torch.zeros(1, 2, 40, device="cuda")
+    dq = torch.full((1, 2, 40, D), 1.5, device="cuda")
+    dk = torch.full((1, 2, 50, D), -2.0, device="cuda")
+    dv = torch.full((1, 2, 50, D), 0.25, device="cuda")
+    # every key after every query: nothing visible, outputs unchanged
+    ra.ra_block_attn_bwd(q, k, k, q, lse, dlt, dq, dk, dv, causal=True, q_pos0=0, k_pos0=1000)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 1.5) and torch.all(dk == -2.0) and torch.all(dv == 0.25)
+    # rows without keys (lse = -inf) contribute nothing either
+    ninf = torch.full((1, 2, 40), float("-inf"), device="cuda")
+    ra.ra_block_attn_bwd(q, k, k, q, ninf, dlt, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 1.5) and torch.all(dk == -2.0) and torch.all(dv == 0.25)
+    e = torch.empty(1, 2, 0, D, device="cuda")
+    ra.ra_block_attn_bwd(e, k, k, e, e[..., 0], e[..., 0], e, dk, dv)  # no-op
+
+
+RING_CASES = [("striped", True, "f32", 16, 4, 64), ("contiguous", True, "f32", 16, 4, 64),
+              ("contiguous", False, "f32", 32, 2, 96), ("striped", True, "bf16", 128, 4, 1024),
+              ("contiguous", True, "bf16", 64, 2, 512)]
+
+
+@pytest.mark.parametrize("lay,causal,dtype,D,N,S", RING_CASES)
+def test_ring_backward_matches_oracle(lay, causal, dtype, D, N, S):
+    gh.say("ra_ring_backward", lay, causal, dtype, D, N, S)
+    Hq, Hkv = 4, 2
+    qn, kn, vn = gh.qkv_global(1, Hq, Hkv, S, D, dtype, seed=41)
+    gn = ra_inputs.normal((1, Hq, S, D), 3, seed=41, dtype=dtype)
+    qs, ks, vs, gs = (gh.shards_on_device(x, N, lay, dtype) for x in (qn, kn, vn, gn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, causal)
+    dq = torch.empty(qs.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    st = ra.ra_ring_backward(qs, ks, vs, o, gs, lse, dq, dk, dv, n_pos=N, layout=lay, causal=causal, stats=True)
+    torch.cuda.synchronize()
+    assert st["block_launches"] == N * N - st["blocks_skipped"]
+    dq_g, dk_g, dv_g = (torch.empty(1, t.shape[2], S, D, device="cuda") for t in (dq, dk, dv))
+    for sh, full in ((dq, dq_g), (dk, dk_g), (dv, dv_g)):
+        ra.ra_stripe_permute(sh, full, layout=lay, inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    want = oracle.attention_grads(qn, kn, vn, gn, causal=causal)
+    mfma = dtype == "bf16" and D in (64, 128)
+    # the backward consumes the GPU forward's bf16 output and fp32 lse, so bf16
+    # rings carry that rounding too
+    tol = 2e-2 if (mfma or dtype == "bf16") else 1e-4
+    for name, got, ref in (("dq", dq_g, want[0]), ("dk", dk_g, want[1]), ("dv", dv_g, want[2])):
+        _close(gh.to_host_f64(got), ref, tol, name)
