@@ -117,6 +117,73 @@ def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2, t
                       f"full causal key range, fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
+def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev):
+    """Time ra_ring_backward over the workload: one forward provides o and lse,
+    then each timed step is the whole backward (delta, every block pair's
+    dQ / dK / dV share).  FLOPs: 10 head_dim per unmasked pair (five products)."""
+    import ra_inputs
+
+    B, Hq, S, D, N, lay = (cfg[k] for k in ("B", "Hq", "S", "D", "N", "layout"))
+    sb = S // N
+    fwd_step(False)
+    if cfg["share"] is not None:
+        t0, ts = (first, N) if lay == "striped" else (first * sb, 1)
+        g_np = ra_inputs.normal((B, Hq, S, D), 3, seed=args.seed, dtype="bf16", t0=t0, t_stride=ts, n_rows=sb)[None]
+    else:
+        g_full = ra_inputs.normal((B, Hq, S, D), 3, seed=args.seed, dtype="bf16")
+        g_np = None
+    if g_np is not None:
+        dout = torch.from_numpy(g_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        gf = torch.from_numpy(g_full.view(np.int16)).view(torch.bfloat16).to(dev)
+        dout = torch.empty_like(q_sh)
+        ra.ra_stripe_permute(gf, dout, layout=lay, inverse=False, n_pos=N)
+        del gf
+    dq = torch.empty(q_sh.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k_sh.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    kw = dict(n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"])
+    log(f"backward warmup {args.warmup}")
+    for _ in range(args.warmup):
+        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw)
+    torch.cuda.synchronize()
+    log(f"backward timing {args.steps} steps")
+    tot = {"block_ms": 0.0, "block_launches": 0, "flops": 0.0}
+    step_ms = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        t_step = time.perf_counter()
+        st = ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, stats=True, **kw)
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - t_step) * 1e3)
+        for key in tot:
+            tot[key] += st[key]
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed / args.steps * 1e3
+    flops_per_step = tot["flops"] / args.steps
+    value = flops_per_step / (ms_per_step * 1e-3) / 1e12
+    per_launch_ms = tot["block_ms"] / max(1, tot["block_launches"])
+    achieved = tot["flops"] / max(1, tot["block_launches"]) / (per_launch_ms * 1e-3) / 1e12
+    line = {
+        "metric": "ring-attention bwd TFLOP/s (causal-adjusted, five products) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": args.workload, "pass": "backward", "batch": B, "q_heads": Hq,
+                   "kv_heads": cfg["Hkv"], "seq_len": S, "head_dim": D, "ring_positions": N, "layout": lay,
+                   "causal": cfg["causal"], "positions_run": n_run, "first_position": first,
+                   "unmasked_flops_per_step": flops_per_step},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "dq_kernel + dkdv_kernel (one block pair)", "launches": tot["block_launches"],
+                     "mean_launch_ms": round(per_launch_ms, 4),
+                     "timing": "HIP events around each block pair's pair of launches"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +193,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the ring backward (dQ, dK, dV) instead of the forward")
     ap.add_argument("--separate-merge", action="store_true",
                     help="fold each block's partial with a separate merge launch instead of in the block kernel")
     args = ap.parse_args()
@@ -198,6 +267,10 @@ def main():
         if o_full is not None:
             ra.ra_stripe_permute(o_sh, o_full, layout=lay, inverse=True, n_pos=N)
         return st
+
+    if args.backward:
+        run_backward(args, cfg, ra, torch, step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev)
+        return
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):

@@ -164,14 +164,15 @@ def attention(q, k, v, causal=False, scale=None, sel_b=None, sel_h=None, sel_t=N
 
 
 def grads(q, k, v, dout, q_pos=None, k_pos=None, causal=False, scale=None, lse=None, delta=None,
-          lib=None):
+          lib=None, key_grads=True):
     """Gradients of one head's attention of query rows q [n, d] over keys k, v [n_keys, d]
     for the upstream gradient dout [n, d] (dtype of q).
 
     lse / delta (fp64 [n], optional): the rows' log-sum-exp and D = dO . O over
     their full key set; given, the result is this key set's share of the
     gradients.  Returns a dict of fp64 arrays dq [n, d], dk, dv [n_keys, d],
-    lse [n], delta [n].
+    lse [n], delta [n]; with key_grads=False the per-key pass is skipped and
+    dk, dv are None.
     """
     q, k, v, dout = (np.ascontiguousarray(x) for x in (q, k, v, dout))
     code = _dtype_code(q)
@@ -187,8 +188,8 @@ def grads(q, k, v, dout, q_pos=None, k_pos=None, causal=False, scale=None, lse=N
         raise ValueError("causal attention needs query positions")
     li = None if lse is None else np.ascontiguousarray(lse, dtype=np.float64)
     di = None if delta is None else np.ascontiguousarray(delta, dtype=np.float64)
-    out = {"dq": np.empty((n, d)), "dk": np.empty((nk, d)), "dv": np.empty((nk, d)),
-           "lse": np.empty(n), "delta": np.empty(n)}
+    out = {"dq": np.empty((n, d)), "dk": np.empty((nk, d)) if key_grads else None,
+           "dv": np.empty((nk, d)) if key_grads else None, "lse": np.empty(n), "delta": np.empty(n)}
     rc = (lib or load()).ra_oracle_grads(
         d, float(scale) if scale else 0.0, int(bool(causal)), code, n, _ptr(q), _ptr(qp), _ptr(dout),
         nk, _ptr(k), _ptr(v), _ptr(kp), _ptr(li), _ptr(di), _ptr(out["dq"]), _ptr(out["dk"]),

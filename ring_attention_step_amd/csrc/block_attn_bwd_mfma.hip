@@ -1,0 +1,485 @@
+// Backward of blockwise attention on bf16 MFMA (gfx950 / CDNA4), fp32 accumulate.
+//
+// The pages run attention's backward pass ("Context Parallelism", Ultralytics
+// glossary, section "Practical use and trade-offs").  For one query block
+// against one key/value block, with the rows' full-key-set lse and
+// delta = dO . O, this block pair's share of the gradients is
+//     p = exp(scale s - lse),  ds = p (dO . v - delta),
+//     dQ += scale ds K,  dK += scale ds^T Q,  dV += p^T dO
+// over visible pairs.  Two kernels, no atomics:
+//
+// dq_kernel -- a wave owns 32 query rows, keys stream through LDS in tiles:
+//     S^T[key, q]  = K . Q^T         (A: K tile, row reads;   B: Q in registers)
+//     dP^T[key, q] = V . dO^T        (A: V tile, row reads;   B: dO in registers)
+//     dS^T = P^T (dP^T - delta), P^T = exp2(S^T scale log2e - lse log2e)
+//     dQ^T[d, q]  += K^T . dS^T      (A: K tile, transposed reads; B: dS^T from
+//                                     the S^T accumulators, converted to bf16)
+// dkdv_kernel -- a wave owns 32 keys, query rows of every query head of the
+// key/value head's group stream through LDS in tiles:
+//     S[q, key]   = Q . K^T          (A: Q tile, row reads;   B: K in registers)
+//     dP[q, key]  = dO . V^T         (A: dO tile, row reads;  B: V in registers)
+//     dV[key, d] += P^T . dO         (A: P^T from the S accumulators; B: dO tile,
+//                                     transposed reads)
+//     dK[key, d] += dS^T . Q         (A: dS^T; B: Q tile, transposed reads)
+// With v_mfma_f32_32x32x16_bf16, lane l supplies row l%32 of A and column
+// l%32 of B as 8 consecutive k-elements from 8(l/32); accumulator register v
+// holds row 8(v/4) + 4(l/32) + v%4, column l%32.  Registers 8kk..8kk+7 of a
+// 32-wide accumulator block therefore hold k-indices 16kk + 8(e/4) + 4h + e%4
+// of the next product; the transposed LDS reads (ds_read_b64_tr_b16) fetch
+// the other operand in exactly that order, so probabilities never leave
+// registers.  Tiles are row-major in LDS with 16-byte chunk c of row r at
+// chunk position c ^ swz(r) (conflict-free for both read kinds on gfx950's 64
+// banks), copied HBM -> LDS by global_load_lds_dwordx4 into double buffers.
+// Two workgroups of four waves share a CU, so one workgroup's MFMAs overlap
+// the other's vector work.
+#include <cmath>
+
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr int kTile = 64;  // keys (dq_kernel) or query rows (dkdv_kernel) per LDS tile
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)((char*)(p)))
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <int D>
+__device__ inline int swz(int r) {
+    if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+__device__ inline bf16x8 pack_bf16x8(const f32x16& x, int base) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const f32x2 f = {x[base + e], x[base + e + 1]};
+        const bf16x2 p = __builtin_convertvector(f, bf16x2);
+        r[e] = p[0];
+        r[e + 1] = p[1];
+    }
+    return r;
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at "no wait").
+__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane HBM -> LDS; lane l's bytes land at lds_base + 16 l.
+// Inline assembly keeps the compiler's wait-count pass from tying operand
+// reads of the current tile to the prefetch of the next; completion is
+// awaited explicitly before the barrier that publishes a tile.
+__device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(offset), "s"(base), "s"(lds_base)
+        : "memory", "m0");
+}
+
+// 4 bytes per lane HBM -> LDS (global_load_lds_dword); lane l's word lands at lds_base + 4 l.
+__device__ inline void lds_dma4(const void* base, uint32_t offset, uint32_t lds_base) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(offset), "s"(base), "s"(lds_base)
+        : "memory", "m0");
+}
+
+__device__ inline bf16x8 ld_row(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
+
+__device__ inline bf16x8 ld_tr(const lds_char* lo, const lds_char* hi) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lo);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)hi);
+    const s16x8 both = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, both);
+}
+
+#define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
+
+// Per-lane LDS byte offsets of both read kinds for a tile of D-element rows.
+template <int D>
+struct TileReads {
+    static constexpr int CPR = D / 8;  // 16-byte chunks per row
+    uint32_t row[D / 16];              // row read: row qi (+32 sub), k-chunk (2 kb + half)
+    uint32_t tr_lo[D / 32], tr_hi[D / 32];
+    __device__ void init(int lane) {
+        const int qi = lane & 31, half = lane >> 5;
+        const int sq = swz<D>(qi);  // rows 32 sub + qi share swz(qi)
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) row[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
+        const int j = lane & 15, dsub = (lane >> 4) & 1;
+        const int vrow = 4 * half + (j >> 2);
+        const int s_lo = swz<D>(vrow), s_hi = swz<D>(vrow + 8);
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+            const int c = 4 * dblk + 2 * dsub + ((j & 3) >> 1);
+            tr_lo[dblk] = (vrow * CPR + (c ^ s_lo)) * 16 + (j & 1) * 8;
+            tr_hi[dblk] = ((vrow + 8) * CPR + (c ^ s_hi)) * 16 + (j & 1) * 8;
+        }
+    }
+    // A/B operand of 32 rows (32 sub ..) x 16 k at k-block kb
+    __device__ bf16x8 rows(const lds_char* tile, int sub, int kb) const {
+        return ld_row(tile + row[kb] + sub * 32 * CPR * 16);
+    }
+    // transposed operand: 32 columns (block dblk) x 16 rows (16 kb2 ..)
+    __device__ bf16x8 cols(const lds_char* tile, int kb2, int dblk) const {
+        const int run = kb2 * 16 * CPR * 16;
+        return ld_tr(tile + tr_lo[dblk] + run, tile + tr_hi[dblk] + run);
+    }
+};
+
+// Tile copy plan: a tile of kTile rows x D bf16 is kTile*D*2/1024 copy
+// instructions of 1 KiB, PER of them for each of the four waves.
+template <int D>
+struct TileCopy {
+    static constexpr int CPR = D / 8;
+    static constexpr int BYTES = kTile * D * 2;
+    static constexpr int PER = BYTES / 1024 / kWaves;
+    int crow[PER], cchunk[PER];
+    __device__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int pos = (wave * PER + i) * 64 + lane;
+            crow[i] = pos / CPR;
+            cchunk[i] = (pos % CPR) ^ swz<D>(crow[i]);
+        }
+    }
+    // rows [r0, r0 + kTile) of src (row stride in elements); rows past n_rows
+    // re-read the last row (finite values, masked later)
+    __device__ void issue(const uint16_t* src, int64_t stride, int r0, int n_rows, uint32_t lds, int wave) const {
+        const uint16_t* base = src + static_cast<int64_t>(r0) * stride;
+        const int last = n_rows - 1 - r0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const uint32_t o = static_cast<uint32_t>(min(crow[i], last) * stride * 2 + cchunk[i] * 16);
+            lds_dma16(base, o, lds + (wave * PER + i) * 1024);
+        }
+    }
+};
+
+// --------------------------------------------------------------------- dQ
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+    const BwdArgs a) {
+    constexpr int kMq = 32 * kWaves;  // query rows per workgroup
+    constexpr int SUB = kTile / 32;
+    constexpr int TB = TileCopy<D>::BYTES;
+    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // {K, V} x 2 buffers
+
+    const int tid = threadIdx.x, lane = tid & 63, qi = lane & 31, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_qt = (a.q_len + kMq - 1) / kMq;
+    int64_t L = blockIdx.x;
+    const int qt_rank = static_cast<int>(L % n_qt);
+    L /= n_qt;
+    const int h = static_cast<int>(L % a.Hq);
+    const int b = static_cast<int>(L / a.Hq);
+    const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
+    const int hk = h / (a.Hq / a.Hkv);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
+    const uint16_t* gp = static_cast<const uint16_t*>(a.dout) + b * a.dos[0] + h * a.dos[1];
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1];
+    const int64_t row0 = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len;
+
+    const int r0 = qt * kMq;
+    const int q0w = r0 + wave * 32;
+    const int row = q0w + qi;
+    const bool row_ok = row < a.q_len;
+
+    bf16x8 qreg[D / 16], greg[D / 16];
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+        qreg[kb] = row_ok ? *reinterpret_cast<const bf16x8*>(qp + row * a.qs[2] + kb * 16 + half * 8) : bf16x8{};
+        greg[kb] = row_ok ? *reinterpret_cast<const bf16x8*>(gp + row * a.dos[2] + kb * 16 + half * 8) : bf16x8{};
+    }
+    const float lse2 = row_ok ? a.lse[row0 + row] * kLog2e : -INFINITY;
+    const float dlt = row_ok ? a.delta[row0 + row] : 0.f;
+    const float c2 = a.scale * kLog2e;
+
+    int key_end = a.kv_len;
+    if (a.causal) key_end = max(0, min(key_end, min(a.q_len - 1, r0 + kMq - 1) + a.mask_offset + 1));
+    const int n_tiles = (key_end + kTile - 1) / kTile;
+    int wave_key_end = 0, wave_full_end = 0;
+    if (q0w < a.q_len) {
+        wave_key_end = wave_full_end = a.kv_len;
+        if (a.causal) {
+            wave_key_end = max(0, min(a.kv_len, min(a.q_len - 1, q0w + 31) + a.mask_offset + 1));
+            wave_full_end = max(0, min(a.kv_len, q0w + a.mask_offset + 1));
+        }
+    }
+
+    TileReads<D> rd;
+    rd.init(lane);
+    TileCopy<D> cp;
+    cp.init(wave, lane);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
+    const lds_char* lds = LDS_PTR(char, smem);
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const uint32_t buf = lds0 + (t & 1) * 2 * TB;
+        cp.issue(kp, a.ks[2], t * kTile, a.kv_len, buf, wave);
+        cp.issue(vp, a.vs[2], t * kTile, a.kv_len, buf + TB, wave);
+    };
+    if (n_tiles > 0) issue(0);
+    for (int t = 0; t < n_tiles; ++t) {
+        wait_vmem_all();
+        __syncthreads();
+        if (t + 1 < n_tiles) issue(t + 1);
+        const int kbase = t * kTile;
+        if (kbase >= wave_key_end) continue;  // nothing this wave sees (wave-uniform)
+        const lds_char* kt = lds + (t & 1) * 2 * TB;
+        const lds_char* vt = kt + TB;
+        f32x16 s[SUB], dp[SUB];
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub) {
+            s[sub] = f32x16{};
+            dp[sub] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < D / 16; ++kb) {
+                s[sub] = MFMA(rd.rows(kt, sub, kb), qreg[kb], s[sub]);
+                dp[sub] = MFMA(rd.rows(vt, sub, kb), greg[kb], dp[sub]);
+            }
+        }
+        const bool edge = kbase + kTile > wave_full_end;  // diagonal or ragged tile
+        bf16x8 dsr[2 * SUB];
+#pragma unroll
+        for (int sub = 0; sub < SUB; ++sub) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                bool vis = lse2 != -INFINITY;
+                if (edge) vis = vis && key < a.kv_len && (!a.causal || key <= row + a.mask_offset);
+                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], c2, -lse2)) : 0.f;
+                s[sub][v] = p * (dp[sub][v] - dlt);
+            }
+            dsr[2 * sub] = pack_bf16x8(s[sub], 0);
+            dsr[2 * sub + 1] = pack_bf16x8(s[sub], 8);
+        }
+#pragma unroll
+        for (int kb2 = 0; kb2 < kTile / 16; ++kb2)
+#pragma unroll
+            for (int dblk = 0; dblk < D / 32; ++dblk) acc[dblk] = MFMA(rd.cols(kt, kb2, dblk), dsr[kb2], acc[dblk]);
+    }
+    wait_vmem_all();
+
+    if (row_ok) {
+        float* out = a.dq + (row0 + row) * D;
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4* dst = reinterpret_cast<f32x4*>(out + dblk * 32 + 8 * g + 4 * half);
+                const f32x4 prev = *dst;
+                *dst = f32x4{__builtin_fmaf(a.scale, acc[dblk][4 * g], prev[0]),
+                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 1], prev[1]),
+                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 2], prev[2]),
+                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 3], prev[3])};
+            }
+    }
+}
+
+// --------------------------------------------------------------------- dK, dV
+// D = 128 holds K, V (B operands) and the dK, dV accumulators in registers,
+// more than two waves per SIMD can have: one wave per SIMD there.
+template <int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+void dkdv_kernel(const BwdArgs a) {
+    constexpr int kMk = 32 * kWaves;  // keys per workgroup
+    constexpr int QB = kTile / 32;    // 32-row query blocks per tile
+    constexpr int TB = TileCopy<D>::BYTES;
+    constexpr int BUF = 2 * TB + 2 * kTile * 4;                     // Q, dO tiles, lse, delta
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];  // two buffers
+
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_kt = (a.kv_len + kMk - 1) / kMk;
+    int64_t L = blockIdx.x;
+    const int kt_rank = static_cast<int>(L % n_kt);
+    L /= n_kt;
+    const int hk = static_cast<int>(L % a.Hkv);
+    const int b = static_cast<int>(L / a.Hkv);
+    const int kt = kt_rank;  // causal: earlier keys see more rows, so these come first
+    const int grp = a.Hq / a.Hkv;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1];
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1];
+
+    const int c0 = kt * kMk;
+    const int c0w = c0 + wave * 32;
+    const int key = c0w + (lane & 31);  // this lane's key (B operand column, accumulator column)
+    const bool key_ok = key < a.kv_len;
+
+    bf16x8 kreg[D / 16], vreg[D / 16];
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) {
+        kreg[kb] = key_ok ? *reinterpret_cast<const bf16x8*>(kp + key * a.ks[2] + kb * 16 + half * 8) : bf16x8{};
+        vreg[kb] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + key * a.vs[2] + kb * 16 + half * 8) : bf16x8{};
+    }
+    const float c2 = a.scale * kLog2e;
+
+    // rows that see some key of this workgroup / this wave, and rows that see all of this wave's keys
+    const int row_start = a.causal ? max(0, min(a.q_len, c0 - a.mask_offset)) : 0;
+    int wave_row_start = a.q_len, wave_row_full = a.q_len;
+    if (c0w < a.kv_len) {
+        wave_row_start = a.causal ? max(0, min(a.q_len, c0w - a.mask_offset)) : 0;
+        wave_row_full = a.causal ? max(0, min(a.q_len, min(a.kv_len - 1, c0w + 31) - a.mask_offset)) : 0;
+    }
+    const int n_tiles = (a.q_len - row_start + kTile - 1) / kTile;
+
+    TileReads<D> rd;
+    rd.init(lane);
+    TileCopy<D> cp;
+    cp.init(wave, lane);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
+    const lds_char* lds = LDS_PTR(char, smem);
+
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
+
+    // one step = one query tile of one head of the group
+    const int n_steps = grp * n_tiles;
+    auto issue = [&](int st) __attribute__((always_inline)) {
+        const int hi = st / n_tiles, t = st % n_tiles;
+        const int h = hk * grp + hi;
+        const int rb = row_start + t * kTile;
+        const uint32_t buf = lds0 + (st & 1) * BUF;
+        cp.issue(static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1], a.qs[2], rb, a.q_len, buf, wave);
+        cp.issue(static_cast<const uint16_t*>(a.dout) + b * a.dos[0] + h * a.dos[1], a.dos[2], rb, a.q_len,
+                  buf + TB, wave);
+    };
+    // lse and delta of the tile's rows, copied like the tiles (rows past the
+    // block re-read its last row; they are masked)
+    auto stats = [&](int st) __attribute__((always_inline)) {
+        const int hi = st / n_tiles, t = st % n_tiles;
+        const int h = hk * grp + hi;
+        const int rb = row_start + t * kTile;
+        const int64_t row0 = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len;
+        const uint32_t dst = lds0 + (st & 1) * BUF + 2 * TB;
+        if (wave == 0) {
+            const uint32_t o = static_cast<uint32_t>(min(rb + lane, a.q_len - 1)) * 4u;
+            lds_dma4(a.lse + row0, o, dst);
+            lds_dma4(a.delta + row0, o, dst + kTile * 4);
+        }
+    };
+    if (n_steps > 0) {
+        issue(0);
+        stats(0);
+    }
+    for (int st = 0; st < n_steps; ++st) {
+        wait_vmem_all();
+        __syncthreads();
+        if (st + 1 < n_steps) {
+            issue(st + 1);
+            stats(st + 1);
+        }
+        const int rb = row_start + (st % n_tiles) * kTile;
+        if (rb + kTile <= wave_row_start) continue;  // no row of this tile sees this wave's keys
+        const lds_char* qt = lds + (st & 1) * BUF;
+        const lds_char* gt = qt + TB;
+        const float* ls = reinterpret_cast<const float*>(smem + (st & 1) * BUF + 2 * TB);
+        const bool edge = rb < wave_row_full || rb + kTile > a.q_len;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < D / 16; ++kb) {
+                s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
+                dp = MFMA(rd.rows(gt, qb, kb), vreg[kb], dp);
+            }
+            // rows of register v: 32 qb + 8 (v/4) + 4 half + v%4 within the tile
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int rt = 32 * qb + 8 * g + 4 * half;
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rt) * kLog2e;  // -inf stays -inf
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + rt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g + e;
+                    const int r = rb + rt + e;
+                    bool vis = key_ok && l4[e] != -INFINITY;
+                    if (edge) vis = vis && r < a.q_len && (!a.causal || key <= r + a.mask_offset);
+                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c2, -l4[e])) : 0.f;
+                    s[v] = p;
+                    dp[v] = p * (dp[v] - d4[e]);
+                }
+            }
+            const bf16x8 p0 = pack_bf16x8(s, 0), p1 = pack_bf16x8(s, 8);
+            const bf16x8 d0 = pack_bf16x8(dp, 0), d1 = pack_bf16x8(dp, 8);
+#pragma unroll
+            for (int dblk = 0; dblk < D / 32; ++dblk) {
+                dv[dblk] = MFMA(p0, rd.cols(gt, 2 * qb, dblk), dv[dblk]);
+                dv[dblk] = MFMA(p1, rd.cols(gt, 2 * qb + 1, dblk), dv[dblk]);
+                dk[dblk] = MFMA(d0, rd.cols(qt, 2 * qb, dblk), dk[dblk]);
+                dk[dblk] = MFMA(d1, rd.cols(qt, 2 * qb + 1, dblk), dk[dblk]);
+            }
+        }
+    }
+    wait_vmem_all();
+
+    // accumulator register v holds key c0w + 8(v/4) + 4 half + v%4, column d = 32 dblk + lane % 32
+    const int64_t kv0 = (static_cast<int64_t>(b) * a.Hkv + hk) * a.kv_len;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int c = c0w + 8 * (v / 4) + 4 * half + (v % 4);
+        if (c >= a.kv_len) continue;
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+            const int64_t o = (kv0 + c) * D + dblk * 32 + (lane & 31);
+            a.dk[o] = __builtin_fmaf(a.scale, dk[dblk][v], a.dk[o]);
+            a.dv[o] += dv[dblk][v];
+        }
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
+    if (dtype != 1 || (a.D != 64 && a.D != 128)) return false;
+    if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.dout) || !aligned16(a.dq) ||
+        !aligned16(a.dk) || !aligned16(a.dv))
+        return false;
+    for (int i = 0; i < 3; ++i)
+        if (a.qs[i] % 8 || a.ks[i] % 8 || a.vs[i] % 8 || a.dos[i] % 8) return false;
+    // per-lane copy offsets within a 64-row tile are 32-bit byte offsets
+    const int64_t lim = int64_t(1) << 24;
+    if (a.qs[2] >= lim || a.ks[2] >= lim || a.vs[2] >= lim || a.dos[2] >= lim) return false;
+    return true;
+}
+
+hipError_t launch_block_bwd_mfma(const BwdArgs& a, hipStream_t s) {
+    if (a.q_len == 0 || a.kv_len == 0) return hipSuccess;
+    const int64_t qb = static_cast<int64_t>((a.q_len + 32 * kWaves - 1) / (32 * kWaves)) * a.Hq * a.B;
+    const int64_t kb = static_cast<int64_t>((a.kv_len + 32 * kWaves - 1) / (32 * kWaves)) * a.Hkv * a.B;
+    if (a.D == 128) {
+        hipLaunchKernelGGL(dq_kernel<128>, dim3(static_cast<unsigned>(qb)), dim3(64 * kWaves), 0, s, a);
+        hipLaunchKernelGGL(dkdv_kernel<128>, dim3(static_cast<unsigned>(kb)), dim3(64 * kWaves), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(dq_kernel<64>, dim3(static_cast<unsigned>(qb)), dim3(64 * kWaves), 0, s, a);
+        hipLaunchKernelGGL(dkdv_kernel<64>, dim3(static_cast<unsigned>(kb)), dim3(64 * kWaves), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ra

@@ -338,7 +338,7 @@ hipError_t launch_block_bwd_simt(const BwdArgs& a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_block_bwd(const BwdArgs& a, int dtype, int force_simt, hipStream_t s) {
-    (void)force_simt;
+    if (!force_simt && bwd_mfma_eligible(a, dtype)) return launch_block_bwd_mfma(a, s);
     return launch_block_bwd_simt(a, dtype, s);
 }
 

@@ -158,3 +158,106 @@ def test_ring_backward_matches_oracle(lay, causal, dtype, D, N, S):
     tol = 2e-2 if (mfma or dtype == "bf16") else 1e-4
     for name, got, ref in (("dq", dq_g, want[0]), ("dk", dk_g, want[1]), ("dv", dv_g, want[2])):
         _close(gh.to_host_f64(got), ref, tol, name)
+
+
+def test_mfma_backward_runs_and_differs_from_vector_path():
+    """bf16 head_dim 128 takes the MFMA kernels (P and dS rounded to bf16 for the
+    products); the vector-ALU path keeps them in fp32.  Both match the oracle,
+    and they are not bit-identical -- so the MFMA path really ran."""
+    gh.say("ra_block_attn_bwd mfma vs simt")
+    B, Hq, Hkv, n, D = 1, 2, 1, 256, 128
+    qn = ra_inputs.normal((B, Hq, n, D), 0, seed=51)
+    kn, vn = (ra_inputs.normal((B, Hkv, n, D), s, seed=51) for s in (1, 2))
+    gn = ra_inputs.normal((B, Hq, n, D), 3, seed=51)
+    q, k, v, g = (gh.to_device(x, "bf16") for x in (qn, kn, vn, gn))
+    pos = np.arange(n)
+    lse = np.empty((B, Hq, n))
+    dlt = np.empty((B, Hq, n))
+    for h in range(Hq):
+        r = oracle.grads(qn[0, h], kn[0, 0], vn[0, 0], gn[0, h], q_pos=pos, causal=True, key_grads=False)
+        lse[0, h], dlt[0, h] = r["lse"], r["delta"]
+    lse_d = torch.from_numpy(lse.astype(np.float32)).cuda()
+    dlt_d = torch.from_numpy(dlt.astype(np.float32)).cuda()
+    outs = []
+    for flags in (0, ra.RA_BLOCK_FORCE_SIMT):
+        dq = torch.zeros(B, Hq, n, D, device="cuda")
+        dk = torch.zeros(B, Hkv, n, D, device="cuda")
+        dv = torch.zeros(B, Hkv, n, D, device="cuda")
+        ra.ra_block_attn_bwd(q, k, v, g, lse_d, dlt_d, dq, dk, dv, causal=True, flags=flags)
+        outs.append((dq, dk, dv))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*outs):
+        assert not torch.equal(a_, b_)
+        assert torch.max(torch.abs(a_ - b_)) <= 2e-2 * max(1.0, float(torch.max(torch.abs(b_))))
+
+
+def test_ring_backward_gqa_moderate_size_all_gradients():
+    gh.say("ra_ring_backward gqa 4096")
+    S, N, Hq, Hkv, D = 4096, 2, 4, 2, 128
+    qn, kn, vn = gh.qkv_global(1, Hq, Hkv, S, D, "bf16", seed=61)
+    gn = ra_inputs.normal((1, Hq, S, D), 3, seed=61)
+    qs, ks, vs, gs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn, gn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    dq = torch.empty(qs.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    ra.ra_ring_backward(qs, ks, vs, o, gs, lse, dq, dk, dv, n_pos=N, layout="striped", causal=True)
+    outs = []
+    for sh in (dq, dk, dv):
+        full = torch.empty(1, sh.shape[2], S, D, device="cuda")
+        ra.ra_stripe_permute(sh, full, layout="striped", inverse=True, n_pos=N)
+        outs.append(full)
+    torch.cuda.synchronize()
+    want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
+    for name, got, ref in zip(("dq", "dk", "dv"), outs, want):
+        _close(gh.to_host_f64(got), ref, 2e-2, name)
+
+
+@pytest.mark.timeout(900)
+def test_backward_256k_share_sampled_rows_and_identities():
+    """The causal 256K striped share at full size: dQ on sampled rows against the
+    oracle, and dK / dV through identities that hold at any size: per key/value
+    head, sum_c dK_c = 0, sum_c dV_c = sum_t dO_t (t over the share's rows), and
+    <Q, dQ> over the group's query heads = <K, dK>."""
+    gh.say("ra_ring_backward 256k share")
+    B, H, S, D, N, i = 1, 8, 262144, 128, 8, 7
+    sb = S // N
+    kn = ra_inputs.normal((B, H, S, D), 1, seed=0)
+    vn = ra_inputs.normal((B, H, S, D), 2, seed=0)
+    qn = ra_inputs.normal((B, H, S, D), 0, seed=0, t0=i, t_stride=N, n_rows=sb)
+    gn = ra_inputs.normal((B, H, S, D), 3, seed=0, t0=i, t_stride=N, n_rows=sb)
+    ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (kn, vn))
+    q, g = gh.to_device(qn, "bf16")[None], gh.to_device(gn, "bf16")[None]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device="cuda")
+    ra.ra_ring_forward(q, ks, vs, o, lse, n_pos=N, first_pos=i, layout="striped", causal=True)
+    dq = torch.empty(q.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    st = ra.ra_ring_backward(q, ks, vs, o, g, lse, dq, dk, dv, n_pos=N, first_pos=i, layout="striped",
+                             causal=True, stats=True)
+    torch.cuda.synchronize()
+    assert st["block_launches"] == N and st["blocks_skipped"] == 0
+    # sampled dQ rows
+    sh, stt = ra_inputs.sample_rows(S, N, 256, heads=H, seed=1)
+    sel = (stt % N) == i
+    sh, stt = sh[sel], stt[sel]
+    rr = (stt - i) // N
+    got = gh.to_host_f64(dq[0, 0][torch.as_tensor(sh, device="cuda"), torch.as_tensor(rr, device="cuda")])
+    want = np.empty_like(got)
+    for h in np.unique(sh):
+        idx = np.nonzero(sh == h)[0]
+        r = oracle.grads(qn[0, h][rr[idx]], kn[0, h], vn[0, h], gn[0, h][rr[idx]], q_pos=stt[idx], causal=True,
+                         key_grads=False)
+        want[idx] = r["dq"]
+    _close(got, want, 2e-2, "dq sampled rows")
+    # identities per head
+    dk_h = dk.double().sum(dim=(0, 3))[0]  # [H, D]: sum over positions and key rows
+    dv_h = dv.double().sum(dim=(0, 3))[0]
+    g_h = g.double().sum(dim=3)[0, 0]      # [H, D]
+    assert float(torch.max(torch.abs(dk_h))) <= 1e-2 * float(dk.abs().double().sum(dim=(0, 3)).max())
+    assert float(torch.max(torch.abs(dv_h - g_h))) <= 1e-2 * float(torch.max(torch.abs(g_h)) + 1.0)
+    qd = (q.double() * dq.double()).sum(dim=(0, 3, 4))[0]         # [H]
+    kd = (ks.double() * dk.double()).sum(dim=(0, 3, 4))[0]        # [H]
+    scale = float(torch.max(torch.abs(qd)).item()) + 1.0
+    assert float(torch.max(torch.abs(qd - kd))) <= 2e-2 * scale
