@@ -112,52 +112,56 @@ __device__ inline bf16x8 ld_tr(const lds_char* lo, const lds_char* hi) {
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
 // Per-lane LDS byte offsets of both read kinds for a tile of D-element rows.
+// Row reads: lane l reads row 32 sub + (l%32), chunk 2 kb + l/32, stored at
+// chunk position (2 kb + h) ^ swz(l%32) = 2 (kb ^ (swz >> 1)) + (h ^ (swz & 1)),
+// i.e. a per-lane base plus 32 (kb ^ x): two registers instead of D/16.
 template <int D>
 struct TileReads {
     static constexpr int CPR = D / 8;  // 16-byte chunks per row
-    uint32_t row[D / 16];              // row read: row qi (+32 sub), k-chunk (2 kb + half)
-    uint32_t tr_lo[D / 32], tr_hi[D / 32];
+    uint32_t row_base, row_x;
+    // Transposed reads: lane l reads chunk c = 4 dblk + c0 (c0 < 4) of rows
+    // vrow and vrow + 8, stored at c ^ swz = 4 (dblk ^ (swz >> 2)) + (c0 ^ (swz & 3)).
+    uint32_t lo_base, lo_x, hi_base, hi_x;
     __device__ void init(int lane) {
         const int qi = lane & 31, half = lane >> 5;
         const int sq = swz<D>(qi);  // rows 32 sub + qi share swz(qi)
-#pragma unroll
-        for (int kb = 0; kb < D / 16; ++kb) row[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
+        row_base = (qi * CPR + (half ^ (sq & 1))) * 16;
+        row_x = static_cast<uint32_t>(sq >> 1);
         const int j = lane & 15, dsub = (lane >> 4) & 1;
         const int vrow = 4 * half + (j >> 2);
         const int s_lo = swz<D>(vrow), s_hi = swz<D>(vrow + 8);
-#pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
-            const int c = 4 * dblk + 2 * dsub + ((j & 3) >> 1);
-            tr_lo[dblk] = (vrow * CPR + (c ^ s_lo)) * 16 + (j & 1) * 8;
-            tr_hi[dblk] = ((vrow + 8) * CPR + (c ^ s_hi)) * 16 + (j & 1) * 8;
-        }
+        const int c0 = 2 * dsub + ((j & 3) >> 1);
+        lo_base = (vrow * CPR + (c0 ^ (s_lo & 3))) * 16 + (j & 1) * 8;
+        hi_base = ((vrow + 8) * CPR + (c0 ^ (s_hi & 3))) * 16 + (j & 1) * 8;
+        lo_x = static_cast<uint32_t>(s_lo >> 2);
+        hi_x = static_cast<uint32_t>(s_hi >> 2);
     }
     // A/B operand of 32 rows (32 sub ..) x 16 k at k-block kb
     __device__ bf16x8 rows(const lds_char* tile, int sub, int kb) const {
-        return ld_row(tile + row[kb] + sub * 32 * CPR * 16);
+        return ld_row(tile + row_base + ((static_cast<uint32_t>(kb) ^ row_x) << 5) + sub * 32 * CPR * 16);
     }
     // transposed operand: 32 columns (block dblk) x 16 rows (16 kb2 ..)
     __device__ bf16x8 cols(const lds_char* tile, int kb2, int dblk) const {
         const int run = kb2 * 16 * CPR * 16;
-        return ld_tr(tile + tr_lo[dblk] + run, tile + tr_hi[dblk] + run);
+        const uint32_t d = static_cast<uint32_t>(dblk);
+        return ld_tr(tile + lo_base + ((d ^ lo_x) << 6) + run, tile + hi_base + ((d ^ hi_x) << 6) + run);
     }
 };
 
 // Tile copy plan: a tile of kTile rows x D bf16 is kTile*D*2/1024 copy
-// instructions of 1 KiB, PER of them for each of the four waves.
+// instructions of 1 KiB, PER of them for each of the four waves.  Instruction
+// i of a wave covers rows crow0 + RPI i (RPI = 64 lanes / CPR chunks a row);
+// lane l fetches the global chunk that belongs at chunk position l % CPR.
 template <int D>
 struct TileCopy {
     static constexpr int CPR = D / 8;
+    static constexpr int RPI = 64 / CPR;
     static constexpr int BYTES = kTile * D * 2;
     static constexpr int PER = BYTES / 1024 / kWaves;
-    int crow[PER], cchunk[PER];
+    int crow0, cpos;
     __device__ void init(int wave, int lane) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int pos = (wave * PER + i) * 64 + lane;
-            crow[i] = pos / CPR;
-            cchunk[i] = (pos % CPR) ^ swz<D>(crow[i]);
-        }
+        crow0 = wave * PER * RPI + lane / CPR;
+        cpos = lane % CPR;
     }
     // rows [r0, r0 + kTile) of src (row stride in elements); rows past n_rows
     // re-read the last row (finite values, masked later)
@@ -166,7 +170,9 @@ struct TileCopy {
         const int last = n_rows - 1 - r0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const uint32_t o = static_cast<uint32_t>(min(crow[i], last) * stride * 2 + cchunk[i] * 16);
+            const int crow = crow0 + RPI * i;
+            const int cchunk = cpos ^ swz<D>(crow);
+            const uint32_t o = static_cast<uint32_t>(min(crow, last) * stride * 2 + cchunk * 16);
             lds_dma16(base, o, lds + (wave * PER + i) * 1024);
         }
     }
@@ -299,11 +305,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // --------------------------------------------------------------------- dK, dV
-// D = 128 holds K, V (B operands) and the dK, dV accumulators in registers,
-// more than two waves per SIMD can have: one wave per SIMD there.
 template <int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
-void dkdv_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
+    const BwdArgs a) {
     constexpr int kMk = 32 * kWaves;  // keys per workgroup
     constexpr int QB = kTile / 32;    // 32-row query blocks per tile
     constexpr int TB = TileCopy<D>::BYTES;
@@ -376,21 +380,25 @@ void dkdv_kernel(const BwdArgs a) {
         const int64_t row0 = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len;
         const uint32_t dst = lds0 + (st & 1) * BUF + 2 * TB;
         if (wave == 0) {
-            const uint32_t o = static_cast<uint32_t>(min(rb + lane, a.q_len - 1)) * 4u;
+            // lane index recomputed here (volatile, so not hoisted and kept live
+            // through the loop, where registers are short)
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            const uint32_t o = static_cast<uint32_t>(min(rb + ln, a.q_len - 1)) * 4u;
             lds_dma4(a.lse + row0, o, dst);
             lds_dma4(a.delta + row0, o, dst + kTile * 4);
         }
     };
     if (n_steps > 0) {
-        issue(0);
         stats(0);
+        issue(0);
     }
     for (int st = 0; st < n_steps; ++st) {
         wait_vmem_all();
         __syncthreads();
         if (st + 1 < n_steps) {
-            issue(st + 1);
             stats(st + 1);
+            issue(st + 1);
         }
         const int rb = row_start + (st % n_tiles) * kTile;
         if (rb + kTile <= wave_row_start) continue;  // no row of this tile sees this wave's keys
@@ -400,35 +408,49 @@ void dkdv_kernel(const BwdArgs a) {
         const bool edge = rb < wave_row_full || rb + kTile > a.q_len;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // S = Q K^T, then P; P^T (bf16) feeds dV at once so that the fp32
+            // scores die before dP is formed
+            f32x16 s = f32x16{};
 #pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) {
-                s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
-                dp = MFMA(rd.rows(gt, qb, kb), vreg[kb], dp);
-            }
+            for (int kb = 0; kb < D / 16; ++kb) s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
             // rows of register v: 32 qb + 8 (v/4) + 4 half + v%4 within the tile
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int rt = 32 * qb + 8 * g + 4 * half;
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rt) * kLog2e;  // -inf stays -inf
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + rt);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
                     const int r = rb + rt + e;
                     bool vis = key_ok && l4[e] != -INFINITY;
                     if (edge) vis = vis && r < a.q_len && (!a.causal || key <= r + a.mask_offset);
-                    const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c2, -l4[e])) : 0.f;
-                    s[v] = p;
-                    dp[v] = p * (dp[v] - d4[e]);
+                    s[v] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c2, -l4[e])) : 0.f;
                 }
             }
             const bf16x8 p0 = pack_bf16x8(s, 0), p1 = pack_bf16x8(s, 8);
-            const bf16x8 d0 = pack_bf16x8(dp, 0), d1 = pack_bf16x8(dp, 8);
 #pragma unroll
             for (int dblk = 0; dblk < D / 32; ++dblk) {
                 dv[dblk] = MFMA(p0, rd.cols(gt, 2 * qb, dblk), dv[dblk]);
                 dv[dblk] = MFMA(p1, rd.cols(gt, 2 * qb + 1, dblk), dv[dblk]);
+            }
+            // dP = dO V^T;  dS = P (dP - delta), with P taken back from its bf16 copy
+            f32x16 dp = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < D / 16; ++kb) dp = MFMA(rd.rows(gt, qb, kb), vreg[kb], dp);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int rt = 32 * qb + 8 * g + 4 * half;
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + rt);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g + e;
+                    const float p = static_cast<float>(v < 8 ? p0[v] : p1[v - 8]);
+                    dp[v] = p * (dp[v] - d4[e]);
+                }
+            }
+            const bf16x8 d0 = pack_bf16x8(dp, 0), d1 = pack_bf16x8(dp, 8);
+#pragma unroll
+            for (int dblk = 0; dblk < D / 32; ++dblk) {
                 dk[dblk] = MFMA(d0, rd.cols(qt, 2 * qb, dblk), dk[dblk]);
                 dk[dblk] = MFMA(d1, rd.cols(qt, 2 * qb + 1, dblk), dk[dblk]);
             }
