@@ -184,6 +184,44 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
     print(json.dumps(line), flush=True)
 
 
+def ring_balance(ra, torch, q_sh, k_sh, v_sh, N, sb, causal, layout_name):
+    """Modeled ring time from measured block-pair times: on a real ring the N
+    positions step in lockstep, so step s lasts as long as the slowest
+    position's block (i - s) mod N; t(i, j) is one ra_block_attn_fwd launch
+    of position i's queries against block j (0 when fully masked).  Returns
+    the modeled time, the perfectly balanced time (sum / N) and their ratio,
+    for the workload's layout and for the other layout of the same tokens."""
+    out = {}
+    lay = layout_name
+    B, Hq, D = q_sh.shape[1], q_sh.shape[2], q_sh.shape[4]
+    o = torch.empty((B, Hq, sb, D), dtype=torch.float32, device=q_sh.device)
+    m = torch.empty((B, Hq, sb), dtype=torch.float32, device=q_sh.device)
+    l = torch.empty_like(m)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name in (lay, "striped" if lay == "contiguous" else "contiguous"):
+        t = np.zeros((N, N))
+        for i in range(N):
+            for j in range(N):
+                off = ra.ra_ring_pair_offset(name, N, sb, i, j)
+                if causal and ra.ra_unmasked_pairs(sb, sb, True, off) == 0:
+                    continue
+                # the mask offset alone decides the work of a pair; the data of the
+                # workload's own shards stands in for the other layout's
+                kw = dict(causal=causal, q_pos0=off, k_pos0=0)
+                ra.ra_block_attn_fwd(q_sh[i], k_sh[j], v_sh[j], o, m, l, **kw)  # warm
+                e0.record()
+                for _ in range(3):
+                    ra.ra_block_attn_fwd(q_sh[i], k_sh[j], v_sh[j], o, m, l, **kw)
+                e1.record()
+                torch.cuda.synchronize()
+                t[i, j] = e0.elapsed_time(e1) / 3
+        steps = [max(t[i, (i - s) % N] for i in range(N)) for s in range(N)]
+        modeled, balanced = float(sum(steps)), float(t.sum() / N)
+        out[name] = {"modeled_ring_ms": round(modeled, 4), "balanced_ms": round(balanced, 4),
+                     "imbalance": round(modeled / balanced, 4) if balanced else None}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +381,11 @@ def main():
                  "mean_launch_ms": round(rt["merge_ms"] / n_merge, 4),
                  "bytes_per_step": merge_bytes}
 
+    balance = None
+    if n_run > 1 and cfg["causal"]:
+        log("ring balance: timing every (position, block) pair")
+        balance = ring_balance(ra, torch, q_sh, k_sh, v_sh, N, sb, cfg["causal"], lay)
+
     cpu = None
     if args.cpu_seconds > 0:
         log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s on all cores, then a third of that on one")
@@ -365,6 +408,7 @@ def main():
                    "merge_schedule": "separate" if args.separate_merge else "fused",
                    "unmasked_flops_per_step": flops_per_step},
         "roofline": roofline, "merge": merge, "cpu_baseline": cpu,
+        "ring_balance": balance,
     }
     print(json.dumps(line), flush=True)
 
