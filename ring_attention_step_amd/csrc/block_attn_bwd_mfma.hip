@@ -34,71 +34,16 @@
 // the other's vector work.
 #include <cmath>
 
+#include "mfma_common.h"
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(8))) short s16x8;
+using namespace mfma;
 
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = 4;
 constexpr int kTile = 64;  // keys (dq_kernel) or query rows (dkdv_kernel) per LDS tile
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)((char*)(p)))
-typedef __attribute__((address_space(3))) char lds_char;
-
-template <int D>
-__device__ inline int swz(int r) {
-    if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
-
-__device__ inline bf16x8 pack_bf16x8(const f32x16& x, int base) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        const f32x2 f = {x[base + e], x[base + e + 1]};
-        const bf16x2 p = __builtin_convertvector(f, bf16x2);
-        r[e] = p[0];
-        r[e + 1] = p[1];
-    }
-    return r;
-}
-
-// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at "no wait").
-__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 16 bytes per lane HBM -> LDS; lane l's bytes land at lds_base + 16 l.
-// Inline assembly keeps the compiler's wait-count pass from tying operand
-// reads of the current tile to the prefetch of the next; completion is
-// awaited explicitly before the barrier that publishes a tile.
-__device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(offset), "s"(base), "s"(lds_base)
-        : "memory", "m0");
-}
-
-// 4 bytes per lane HBM -> LDS (global_load_lds_dword); lane l's word lands at lds_base + 4 l.
-__device__ inline void lds_dma4(const void* base, uint32_t offset, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dword %0, %1"
-        :
-        : "v"(offset), "s"(base), "s"(lds_base)
-        : "memory", "m0");
-}
 
 __device__ inline bf16x8 ld_row(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
 
@@ -234,8 +179,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
     rd.init(lane);
     TileCopy<D> cp;
     cp.init(wave, lane);
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
-    const lds_char* lds = LDS_PTR(char, smem);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
+    const lds_char* lds = RA_LDS_PTR(char, smem);
 
     f32x16 acc[D / 32];
 #pragma unroll
@@ -353,8 +298,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
     rd.init(lane);
     TileCopy<D> cp;
     cp.init(wave, lane);
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
-    const lds_char* lds = LDS_PTR(char, smem);
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
+    const lds_char* lds = RA_LDS_PTR(char, smem);
 
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll

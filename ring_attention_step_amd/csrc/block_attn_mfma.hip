@@ -58,18 +58,13 @@
 // workgroups land on the same XCD (shared L2 for K/V).
 #include <cmath>
 
+#include "mfma_common.h"
 #include "ra_internal.h"
 
 namespace ra {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(8))) short s16x8;
+using namespace mfma;
 
 // Compile-time tuning knobs (defaults are the measured best on gfx950).
 #ifndef RA_MFMA_NK
@@ -89,21 +84,7 @@ typedef __attribute__((ext_vector_type(8))) short s16x8;
 #endif
 constexpr int kNk = RA_MFMA_NK;  // keys per tile (64 or 128)
 constexpr int kSub = kNk / 32;   // 32-key sub-tiles per tile
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 8.0f;  // lazy-rescale threshold, log2 units
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)((char*)(p)))
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Chunk-position permutation of tile rows (see the data-movement note).
-// D = 128: 16 chunks a row, swap the two 2-bit fields of r & 15.
-// D = 64: 8 chunks a row (two rows per 64-bank line), bits 1..3 of r.
-template <int D>
-__device__ inline int swz(int r) {
-    if (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
-    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
-}
 
 // Maximum with NaN propagation (IEEE 754-2019 maximum).  Unlike fmaxf it needs
 // no quieting of its operands first, and two of them fuse into one
@@ -151,38 +132,6 @@ __device__ inline float xhalf_sum(float x) {
 __device__ inline int64_t xcd_remap(int64_t w, int64_t n) {
     const int64_t q = n / 8, r = n % 8, x = w % 8, i = w / 8;
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
-}
-
-__device__ inline bf16x8 pack_bf16x8(const f32x16& x, int base) {
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-        const f32x2 f = {x[base + e], x[base + e + 1]};
-        const bf16x2 p = __builtin_convertvector(f, bf16x2);
-        r[e] = p[0];
-        r[e + 1] = p[1];
-    }
-    return r;
-}
-
-// s_waitcnt vmcnt(0) (gfx9 encoding: expcnt and lgkmcnt left at "no wait").
-__device__ inline void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 16 bytes per lane HBM -> LDS (global_load_lds_dwordx4): lane l's bytes land at
-// LDS byte address lds_base + 16 l.  Issued from inline assembly so that the
-// compiler's wait-count pass does not treat the prefetch of the next tile as a
-// hazard for reads of the current one; completion is awaited explicitly
-// (wait_vmem_all) before the barrier that publishes a tile.
-// The address is a wave-uniform base (SGPR pair) plus a 32-bit per-lane
-// byte offset, so no per-lane 64-bit arithmetic is needed.
-__device__ inline void lds_dma16(const void* base, uint32_t offset, uint32_t lds_base) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(offset), "s"(base), "s"(lds_base)
-        : "memory", "m0");
 }
 
 // Two waves per SIMD (<= 256 registers): one wave's MFMAs overlap the other's
@@ -252,7 +201,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // chunk that belongs at its position.  Rows past the block re-read its last
     // row (finite values; they are masked).
     const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(char, smem)));
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     // per-lane byte offsets of this wave's copy instructions within a full tile
     uint32_t kcp[PER_WAVE], vcp[PER_WAVE];
     int crow[PER_WAVE], cchunk[PER_WAVE];
@@ -296,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     for (int i = 0; i < PER_G; ++i) cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
 
     // per-lane LDS byte offsets of the operand reads
-    const lds_char* lds = LDS_PTR(char, smem);
+    const lds_char* lds = RA_LDS_PTR(char, smem);
     const int sq = swz<D>(qi);  // K rows sub*32 + qi share swz(qi)
     uint32_t koff[D / 16];
 #pragma unroll

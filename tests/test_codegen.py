@@ -3,12 +3,13 @@ hipcc cross-compiles the sources here and the AMD assembly is inspected).
 
 * No packed fp32 arithmetic (v_pk_fma_f32 / v_pk_mul_f32 / v_pk_add_f32) in
   any kernel: every source is built with the packed-fp32 feature disabled.
-* The bf16 MFMA kernel keeps everything in registers (no scratch) at two waves
-  per SIMD: a scratch access inside its main loop would make the compiler
-  wait for all outstanding vector-memory operations, including the untracked
-  LDS-DMA prefetch of the next tile.
-* m0 is written only by the LDS-DMA helper (the compiler must not rely on m0
-  anywhere in that kernel, since the helper's inline assembly clobbers it).
+* The bf16 MFMA kernels (forward, and the backward's dQ and dK/dV) keep
+  everything in registers (no scratch) at two waves per SIMD: a scratch
+  access inside a main loop would make the compiler wait for all outstanding
+  vector-memory operations, including the untracked LDS-DMA prefetch of the
+  next tile.
+* m0 is written only by the LDS-DMA helpers (the compiler must not rely on m0
+  anywhere in those kernels, since the helpers' inline assembly clobbers it).
 """
 import glob
 import os
@@ -38,21 +39,23 @@ def test_no_packed_fp32_instructions(src, tmp_path):
     assert not bad, f"{os.path.basename(src)} contains packed fp32 instructions: {sorted(set(bad))}"
 
 
-def _kernels(asm):
-    """Split device assembly into {symbol: body} for each kernel."""
+def _kernels(asm, pattern=r"block_mfma_kernel"):
+    """Split device assembly into {symbol: body} for each kernel matching pattern."""
     out = {}
-    for m in re.finditer(r"^(_Z\S*block_mfma_kernel\S*):", asm, flags=re.M):
+    for m in re.finditer(r"^(_Z\S*(?:" + pattern + r")\S*):", asm, flags=re.M):
         start = m.end()
         end = asm.find(".Lfunc_end", start)
         out[m.group(1)] = asm[start:end]
     return out
 
 
-def test_mfma_kernel_registers_scratch_and_m0(tmp_path):
-    src = os.path.join(B.CSRC, "block_attn_mfma.hip")
+@pytest.mark.parametrize("src,pattern,count", [("block_attn_mfma.hip", "block_mfma_kernel", 2),
+                                               ("block_attn_bwd_mfma.hip", "dq_kernel|dkdv_kernel", 4)])
+def test_mfma_kernel_registers_scratch_and_m0(tmp_path, src, pattern, count):
+    src = os.path.join(B.CSRC, src)
     asm = _device_asm(src, tmp_path)
-    kernels = _kernels(asm)
-    assert len(kernels) == 2, "expected the head_dim 64 and 128 instantiations"
+    kernels = _kernels(asm, pattern)
+    assert len(kernels) == count, "expected the head_dim 64 and 128 instantiations"
     for name, body in kernels.items():
         for line in body.splitlines():
             code = line.split(";")[0]
