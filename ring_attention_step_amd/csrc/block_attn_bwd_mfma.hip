@@ -31,7 +31,8 @@
 // chunk position c ^ swz(r) (conflict-free for both read kinds on gfx950's 64
 // banks), copied HBM -> LDS by global_load_lds_dwordx4 into double buffers.
 // Two workgroups of four waves share a CU, so one workgroup's MFMAs overlap
-// the other's vector work.
+// the other's vector work (eight-wave workgroups sharing each tile measured
+// slower).
 #include <cmath>
 
 #include "mfma_common.h"
@@ -42,7 +43,15 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 4;
+// Waves per workgroup of each kernel (compile-time knobs; defaults measured best).
+#ifndef RA_BWD_DQ_WAVES
+#define RA_BWD_DQ_WAVES 4
+#endif
+#ifndef RA_BWD_KV_WAVES
+#define RA_BWD_KV_WAVES 4
+#endif
+constexpr int kDqWaves = RA_BWD_DQ_WAVES;
+constexpr int kKvWaves = RA_BWD_KV_WAVES;
 constexpr int kTile = 64;  // keys (dq_kernel) or query rows (dkdv_kernel) per LDS tile
 
 __device__ inline bf16x8 ld_row(const lds_char* p) { return *(const __attribute__((address_space(3))) bf16x8*)p; }
@@ -94,15 +103,15 @@ struct TileReads {
 };
 
 // Tile copy plan: a tile of kTile rows x D bf16 is kTile*D*2/1024 copy
-// instructions of 1 KiB, PER of them for each of the four waves.  Instruction
+// instructions of 1 KiB, PER of them for each of the WAVES waves.  Instruction
 // i of a wave covers rows crow0 + RPI i (RPI = 64 lanes / CPR chunks a row);
 // lane l fetches the global chunk that belongs at chunk position l % CPR.
-template <int D>
+template <int D, int WAVES>
 struct TileCopy {
     static constexpr int CPR = D / 8;
     static constexpr int RPI = 64 / CPR;
     static constexpr int BYTES = kTile * D * 2;
-    static constexpr int PER = BYTES / 1024 / kWaves;
+    static constexpr int PER = BYTES / 1024 / WAVES;
     int crow0, cpos;
     __device__ void init(int wave, int lane) {
         crow0 = wave * PER * RPI + lane / CPR;
@@ -125,11 +134,11 @@ struct TileCopy {
 
 // --------------------------------------------------------------------- dQ
 template <int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
     const BwdArgs a) {
-    constexpr int kMq = 32 * kWaves;  // query rows per workgroup
+    constexpr int kMq = 32 * kDqWaves;  // query rows per workgroup
     constexpr int SUB = kTile / 32;
-    constexpr int TB = TileCopy<D>::BYTES;
+    constexpr int TB = TileCopy<D, kDqWaves>::BYTES;
     __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // {K, V} x 2 buffers
 
     const int tid = threadIdx.x, lane = tid & 63, qi = lane & 31, half = lane >> 5;
@@ -177,7 +186,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 
     TileReads<D> rd;
     rd.init(lane);
-    TileCopy<D> cp;
+    TileCopy<D, kDqWaves> cp;
     cp.init(wave, lane);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     const lds_char* lds = RA_LDS_PTR(char, smem);
@@ -251,11 +260,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 
 // --------------------------------------------------------------------- dK, dV
 template <int D>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
+__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     const BwdArgs a) {
-    constexpr int kMk = 32 * kWaves;  // keys per workgroup
+    constexpr int kMk = 32 * kKvWaves;  // keys per workgroup
     constexpr int QB = kTile / 32;    // 32-row query blocks per tile
-    constexpr int TB = TileCopy<D>::BYTES;
+    constexpr int TB = TileCopy<D, kKvWaves>::BYTES;
     constexpr int BUF = 2 * TB + 2 * kTile * 4;                     // Q, dO tiles, lse, delta
     __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];  // two buffers
 
@@ -296,7 +305,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 
 
     TileReads<D> rd;
     rd.init(lane);
-    TileCopy<D> cp;
+    TileCopy<D, kKvWaves> cp;
     cp.init(wave, lane);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     const lds_char* lds = RA_LDS_PTR(char, smem);
@@ -437,14 +446,14 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
 
 hipError_t launch_block_bwd_mfma(const BwdArgs& a, hipStream_t s) {
     if (a.q_len == 0 || a.kv_len == 0) return hipSuccess;
-    const int64_t qb = static_cast<int64_t>((a.q_len + 32 * kWaves - 1) / (32 * kWaves)) * a.Hq * a.B;
-    const int64_t kb = static_cast<int64_t>((a.kv_len + 32 * kWaves - 1) / (32 * kWaves)) * a.Hkv * a.B;
+    const int64_t qb = static_cast<int64_t>((a.q_len + 32 * kDqWaves - 1) / (32 * kDqWaves)) * a.Hq * a.B;
+    const int64_t kb = static_cast<int64_t>((a.kv_len + 32 * kKvWaves - 1) / (32 * kKvWaves)) * a.Hkv * a.B;
     if (a.D == 128) {
-        hipLaunchKernelGGL(dq_kernel<128>, dim3(static_cast<unsigned>(qb)), dim3(64 * kWaves), 0, s, a);
-        hipLaunchKernelGGL(dkdv_kernel<128>, dim3(static_cast<unsigned>(kb)), dim3(64 * kWaves), 0, s, a);
+        hipLaunchKernelGGL(dq_kernel<128>, dim3(static_cast<unsigned>(qb)), dim3(64 * kDqWaves), 0, s, a);
+        hipLaunchKernelGGL(dkdv_kernel<128>, dim3(static_cast<unsigned>(kb)), dim3(64 * kKvWaves), 0, s, a);
     } else {
-        hipLaunchKernelGGL(dq_kernel<64>, dim3(static_cast<unsigned>(qb)), dim3(64 * kWaves), 0, s, a);
-        hipLaunchKernelGGL(dkdv_kernel<64>, dim3(static_cast<unsigned>(kb)), dim3(64 * kWaves), 0, s, a);
+        hipLaunchKernelGGL(dq_kernel<64>, dim3(static_cast<unsigned>(qb)), dim3(64 * kDqWaves), 0, s, a);
+        hipLaunchKernelGGL(dkdv_kernel<64>, dim3(static_cast<unsigned>(kb)), dim3(64 * kKvWaves), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -261,3 +261,35 @@ def test_backward_256k_share_sampled_rows_and_identities():
     kd = (ks.double() * dk.double()).sum(dim=(0, 3, 4))[0]        # [H]
     scale = float(torch.max(torch.abs(qd)).item()) + 1.0
     assert float(torch.max(torch.abs(qd - kd))) <= 2e-2 * scale
+
+
+@pytest.mark.parametrize("lay", ["striped", "contiguous"])
+def test_batch2_gqa4_ring_forward_and_backward(lay):
+    """Batch 2, 8 query heads on 2 key/value heads, d 64: forward output and lse
+    on every row, and all three gradients, against the oracle."""
+    gh.say("ring batch 2 gqa 4", lay)
+    B, Hq, Hkv, S, D, N = 2, 8, 2, 512, 64, 4
+    qn, kn, vn = gh.qkv_global(B, Hq, Hkv, S, D, "bf16", seed=71)
+    gn = ra_inputs.normal((B, Hq, S, D), 3, seed=71)
+    qs, ks, vs, gs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn, gn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
+    o_full = torch.empty(B, Hq, S, D, device="cuda", dtype=torch.bfloat16)
+    ra.ra_stripe_permute(o, o_full, layout=lay, inverse=True, n_pos=N)
+    lse_full = torch.empty(B, Hq, S, 1, device="cuda")
+    ra.ra_stripe_permute(lse[..., None].contiguous(), lse_full, layout=lay, inverse=True, n_pos=N)
+    dq = torch.empty(qs.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    ra.ra_ring_backward(qs, ks, vs, o, gs, lse, dq, dk, dv, n_pos=N, layout=lay, causal=True)
+    grads = []
+    for sh in (dq, dk, dv):
+        full = torch.empty(B, sh.shape[2], S, D, device="cuda")
+        ra.ra_stripe_permute(sh, full, layout=lay, inverse=True, n_pos=N)
+        grads.append(full)
+    torch.cuda.synchronize()
+    want_o, want_lse = oracle.attention(qn, kn, vn, causal=True)
+    assert np.max(np.abs(gh.to_host_f64(o_full) - want_o)) <= gh.TOL["bf16"]["o"]
+    assert np.max(np.abs(gh.to_host_f64(lse_full)[..., 0] - want_lse)) <= gh.TOL["bf16"]["lse"]
+    want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
+    for name, got, ref in zip(("dq", "dk", "dv"), grads, want):
+        _close(gh.to_host_f64(got), ref, 2e-2, name)
