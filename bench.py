@@ -148,19 +148,24 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
         ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw)
     torch.cuda.synchronize()
     log(f"backward timing {args.steps} steps")
-    tot = {"block_ms": 0.0, "block_launches": 0, "flops": 0.0}
-    step_ms = []
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
-        t_step = time.perf_counter()
+    for e0, e1 in marks:
+        e0.record()
+        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw)
+        e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in marks]
+    ms_per_step = elapsed / args.steps * 1e3
+    # launch timing (HIP events around every block pair) in 3 more steps
+    tot = {"block_ms": 0.0, "block_launches": 0, "flops": 0.0}
+    for _ in range(3):
         st = ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, stats=True, **kw)
-        torch.cuda.synchronize()
-        step_ms.append((time.perf_counter() - t_step) * 1e3)
         for key in tot:
             tot[key] += st[key]
-    elapsed = time.perf_counter() - t_start
-    ms_per_step = elapsed / args.steps * 1e3
-    flops_per_step = tot["flops"] / args.steps
+    flops_per_step = tot["flops"] / 3
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     per_launch_ms = tot["block_ms"] / max(1, tot["block_launches"])
     achieved = tot["flops"] / max(1, tot["block_launches"]) / (per_launch_ms * 1e-3) / 1e12
@@ -178,7 +183,8 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "kernel": "dq_kernel + dkdv_kernel (one block pair)", "launches": tot["block_launches"],
                      "mean_launch_ms": round(per_launch_ms, 4),
-                     "timing": "HIP events around each block pair's pair of launches"},
+                     "timing": "HIP events around each block pair's pair of launches, 3 steps after the "
+                               "timed ones"},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -235,6 +241,10 @@ def main():
                     help="time the ring backward (dQ, dK, dV) instead of the forward")
     ap.add_argument("--separate-merge", action="store_true",
                     help="fold each block's partial with a separate merge launch instead of in the block kernel")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (launch overhead removed)")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="key ranges per block launch (0: the library's automatic choice, 1: none)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring positions are virtual positions on a single "
@@ -291,8 +301,9 @@ def main():
     lse = torch.empty(q_sh.shape[:4], dtype=torch.float32, device=dev)
     o_full = torch.empty((B, Hq, S, D), dtype=torch.bfloat16, device=dev) if q_g is not None else None
     desc = ra.ring_desc(q_sh, k_sh, n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"],
-                        separate_merge=args.separate_merge)
+                        separate_merge=args.separate_merge, kv_splits=args.kv_splits)
     workspace = torch.empty(ra.ra_ring_workspace_size(desc), dtype=torch.uint8, device=dev)
+    kv_splits = args.kv_splits
 
     def step(stats, n_streams=0):
         ra.ra_stripe_permute(k_g, k_sh, layout=lay, inverse=False, n_pos=N)
@@ -301,7 +312,7 @@ def main():
             ra.ra_stripe_permute(q_g, q_sh, layout=lay, inverse=False, n_pos=N)
         st = ra.ra_ring_forward(q_sh, k_sh, v_sh, o_sh, lse, n_pos=N, first_pos=first, layout=lay,
                                 causal=cfg["causal"], workspace=workspace, stats=stats,
-                                separate_merge=args.separate_merge, n_streams=n_streams)
+                                separate_merge=args.separate_merge, n_streams=n_streams, kv_splits=kv_splits)
         if o_full is not None:
             ra.ra_stripe_permute(o_sh, o_full, layout=lay, inverse=True, n_pos=N)
         return st
@@ -314,36 +325,63 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    totals = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
-    step_ms = []
-    t_start = time.perf_counter()
-    for _ in range(args.steps):
-        t_step = time.perf_counter()
-        st = step(True)
+    # the step's work accounting (FLOPs, key ranges) from one untimed step
+    st = step(True)
+    torch.cuda.synchronize()
+    flops_per_step = st["flops"]
+    splits = int(st["kv_splits"])  # key ranges per block launch
+    run_step = step
+    if args.graph:  # the library's streams and events exist after the eager steps above
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(False)
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        step_ms.append((time.perf_counter() - t_step) * 1e3)
-        for key in totals:
-            totals[key] += st[key]
+        with torch.cuda.graph(graph):
+            step(False)
+        torch.cuda.synchronize()
+
+        def run_step(_stats):
+            graph.replay()
+    log(f"timing {args.steps} steps")
+    # steps are enqueued back to back; events on the caller's stream (which
+    # every step's work joins) give per-step times without a host round trip
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in marks:
+        e0.record()
+        run_step(False)
+        e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in marks]
     ms_per_step = elapsed / args.steps * 1e3
-    flops_per_step = totals["flops"] / args.steps
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     log(f"{ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
     # block-attention kernel roofline: algorithmic FLOPs per launch / mean launch
-    # time.  A full ring runs its positions on several streams, where launches
+    # time, from HIP events around every launch in 3 steps after the timed
+    # region.  A full ring runs its positions on several streams, where launches
     # overlap and event spans overstate each one; its launches are then timed
-    # in a few extra steps on one stream, after the timed region.
-    rt = totals
+    # on one stream, with the key ranges of the timed steps.
+    n_stat = 3
+    rt = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
+    stat_streams = 0
     if n_run > 1:
-        rt = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
-        for _ in range(3):
-            st = step(True, n_streams=1)
-            for key in rt:
-                rt[key] += st[key]
-        torch.cuda.synchronize()
+        stat_streams = 1
+        kv_splits = splits  # whatever one stream alone would choose
+        if splits > 1:
+            workspace = torch.empty(ra.ra_ring_workspace_size(ra.ring_desc(
+                q_sh, k_sh, n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"], n_streams=1,
+                kv_splits=splits)), dtype=torch.uint8, device=dev)
+    for _ in range(n_stat):
+        st = step(True, n_streams=stat_streams)
+        for key in rt:
+            rt[key] += st[key]
+    torch.cuda.synchronize()
     per_launch_flops = rt["flops"] / max(1, rt["block_launches"])
     per_launch_ms = rt["block_ms"] / max(1, rt["block_launches"])
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
@@ -352,30 +390,35 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",
                 "launches": rt["block_launches"], "mean_launch_ms": round(per_launch_ms, 4),
-                "timing": "HIP events around each launch on its stream" +
-                          (" (3 extra steps on one stream)" if n_run > 1 else "")}
+                "timing": "HIP events around each launch on its stream, 3 steps after the timed ones" +
+                          (" (on one stream)" if n_run > 1 else "")}
 
-    # merge kernel: algorithmic bytes per step.  Fused schedule (default): the
-    # block kernel folds each partial into the running state, and the merge
-    # kernel only finalises (read fp32 O, m, l; write the bf16 output and the
-    # log-sum-exp: 4 D + 8 + 2 D + 4 bytes a row).  Separate schedule: per
-    # position with c computed blocks, c - 2 plain folds (read two states, write
-    # one: 12 D + 24 bytes a row) and one fold that finalises (8 D + 16 + 2 D + 4).
+    # merge kernel: algorithmic bytes per step.  A state (fp32 O, m, l) is
+    # 4 D + 8 bytes a row, a finalised row (bf16 output, log-sum-exp) 2 D + 4.
+    # Fused schedule: the block kernel folds each partial into the running
+    # state, and the merge kernel only finalises (read a state, write a row).
+    # Separate schedule: per position with c computed blocks, c - 2 plain folds
+    # (read two states, write one) and one fold that finalises.  Key splits
+    # (n ranges): every computed block's fold reads n partials and the running
+    # state (none at the first), and writes the state (or, at the last, a row).
     rows_pos = B * Hq * sb
+    st_b, row_b = 4 * D + 8, 2 * D + 4
     merge_bytes = 0
     for p in range(n_run):
         c = sum(1 for j in range(N)
                 if not (cfg["causal"] and ra.ra_unmasked_pairs(
                     sb, sb, True, ra.ra_ring_pair_offset(lay, N, sb, first + p, j)) == 0))
-        if c == 1 or not args.separate_merge:
-            merge_bytes += rows_pos * (4 * D + 8 + 2 * D + 4)
+        if splits > 1:
+            for s_i in range(c):
+                merge_bytes += rows_pos * (splits * st_b + (st_b if s_i else 0) + (row_b if s_i == c - 1 else st_b))
+        elif c == 1 or not args.separate_merge:
+            merge_bytes += rows_pos * (st_b + row_b)
         else:
-            merge_bytes += (c - 2) * rows_pos * (12 * D + 24) + rows_pos * (8 * D + 16 + 2 * D + 4)
+            merge_bytes += (c - 2) * rows_pos * 3 * st_b + rows_pos * (2 * st_b + row_b)
     n_merge = rt["merge_launches"]
     merge = None
     if n_merge:
-        n_steps = 3 if n_run > 1 else args.steps
-        gbps = merge_bytes * n_steps / (rt["merge_ms"] * 1e-3) / 1e9
+        gbps = merge_bytes * n_stat / (rt["merge_ms"] * 1e-3) / 1e9
         merge = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                  "frac": round(gbps / PEAK_HBM_GBPS, 4), "launches": n_merge,
                  "mean_launch_ms": round(rt["merge_ms"] / n_merge, 4),
@@ -405,7 +448,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
                    "head_dim": D, "ring_positions": N, "layout": lay, "causal": cfg["causal"],
                    "positions_run": n_run, "first_position": first,
-                   "merge_schedule": "separate" if args.separate_merge else "fused",
+                   "merge_schedule": "separate" if args.separate_merge else "fused", "kv_splits": splits,
+                   "launch": "hip graph replay" if args.graph else "eager",
                    "unmasked_flops_per_step": flops_per_step},
         "roofline": roofline, "merge": merge, "cpu_baseline": cpu,
         "ring_balance": balance,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 3
+#define RA_ABI_VERSION 4
 
 typedef enum ra_status {
     RA_OK = 0,
@@ -156,6 +156,7 @@ typedef struct ra_ring_stats {
     double unmasked_pairs;              /* (query row, key) pairs attended, all heads   */
     double flops;                       /* ra_ring_forward: 4 * head_dim * unmasked_pairs;
                                            ra_ring_backward: 10 * head_dim * unmasked_pairs */
+    int64_t kv_splits;                  /* ra_ring_forward: key ranges per block launch (1: none) */
 } ra_ring_stats;
 
 /*
@@ -190,6 +191,15 @@ typedef struct ra_ring_desc {
                                ra_lse_merge pass ends the position;
                                1: each step writes a partial and ra_lse_merge
                                folds it in (the last fold also finalises)     */
+    int32_t kv_splits;  /* fused schedule, bf16, head_dim 64 or 128 only: each
+                           block launch cuts the block's keys into this many
+                           ranges (one workgroup per query tile, head and
+                           range), and one ra_lse_merge pass per step folds
+                           the ranges' partials into the running state.
+                           0: automatic (used when a step's launches would
+                           fill fewer workgroups than the GPU has compute
+                           units); 1: off; 2..8: that many ranges (capped at
+                           the block's 128-key tiles).  Ignored otherwise.   */
     const int32_t* visit_order; /* host array [n_pos] (a permutation) or NULL     */
     ra_ring_stats* stats;       /* host pointer or NULL.  When set, every launch is
                                    timed with HIP events and the call waits for
@@ -218,6 +228,11 @@ ra_status ra_ring_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * All dense, position-major (the layout ra_stripe_permute produces).
  * workspace: device memory of at least ra_ring_workspace_size bytes.
  * Concurrent calls are serialised on an internal mutex.
+ * With stats == NULL the call only enqueues work -- kernel launches, event
+ * records and waits (and, with emulate_copy, device-to-device copies) -- on
+ * `stream` and on library streams forked from it and joined back, so it may
+ * be captured into a HIP graph once an eager call with the same n_streams has
+ * created those streams and events on the device.
  */
 ra_status ra_ring_forward(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
                           void* o, float* lse, void* workspace, size_t workspace_bytes,

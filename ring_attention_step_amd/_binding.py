@@ -42,7 +42,7 @@ class ra_ring_stats(ctypes.Structure):
     _fields_ = [("block_ms", ctypes.c_double), ("merge_ms", ctypes.c_double), ("copy_ms", ctypes.c_double),
                 ("block_launches", ctypes.c_int64), ("merge_launches", ctypes.c_int64),
                 ("copy_launches", ctypes.c_int64), ("blocks_skipped", ctypes.c_int64),
-                ("unmasked_pairs", ctypes.c_double), ("flops", ctypes.c_double)]
+                ("unmasked_pairs", ctypes.c_double), ("flops", ctypes.c_double), ("kv_splits", ctypes.c_int64)]
 
 
 class ra_ring_desc(ctypes.Structure):
@@ -51,7 +51,7 @@ class ra_ring_desc(ctypes.Structure):
                 ("n_run", ctypes.c_int32), ("layout", ctypes.c_int32), ("block_len", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("emulate_copy", ctypes.c_int32), ("n_streams", ctypes.c_int32),
-                ("separate_merge", ctypes.c_int32),
+                ("separate_merge", ctypes.c_int32), ("kv_splits", ctypes.c_int32),
                 ("visit_order", ctypes.POINTER(ctypes.c_int32)),
                 ("stats", ctypes.POINTER(ra_ring_stats))]
 
@@ -223,7 +223,7 @@ def ra_lse_merge(o_acc, m_acc, l_acc, o_part=None, m_part=None, l_part=None, o_o
 
 
 def ring_desc(q, k, *, n_pos, first_pos=0, layout="contiguous", causal=False, scale=0.0, emulate_copy=False,
-              n_streams=0, separate_merge=False, visit_order=None, stats=None):
+              n_streams=0, separate_merge=False, kv_splits=0, visit_order=None, stats=None):
     """ra_ring_desc for q [n_run, B, Hq, Sb, D] and k [n_pos, B, Hkv, Sb, D]."""
     n_run, B, Hq, Sb, D = q.shape
     if k.shape[0] != n_pos or k.shape[1] != B or k.shape[3] != Sb or k.shape[4] != D:
@@ -235,6 +235,7 @@ def ring_desc(q, k, *, n_pos, first_pos=0, layout="contiguous", causal=False, sc
     d.block_len, d.dtype, d.causal, d.scale = Sb, _dtype(q), int(bool(causal)), float(scale)
     d.emulate_copy, d.n_streams = int(bool(emulate_copy)), int(n_streams)
     d.separate_merge = int(bool(separate_merge))
+    d.kv_splits = int(kv_splits)
     if visit_order is not None:
         arr = (ctypes.c_int32 * n_pos)(*[int(x) for x in visit_order])
         d._order_keepalive = arr
@@ -251,8 +252,8 @@ def ra_ring_workspace_size(desc) -> int:
 
 
 def ra_ring_forward(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contiguous", causal=False,
-                    scale=0.0, emulate_copy=False, n_streams=0, separate_merge=False, visit_order=None,
-                    workspace=None, stats=False, stream=None):
+                    scale=0.0, emulate_copy=False, n_streams=0, separate_merge=False, kv_splits=0,
+                    visit_order=None, workspace=None, stats=False, stream=None):
     """Run positions first_pos .. first_pos + n_run - 1 of an n_pos ring on one GPU.
 
     Returns a dict of ra_ring_stats when stats=True (the call then waits for its
@@ -266,7 +267,7 @@ def ra_ring_forward(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contigu
     st = ra_ring_stats() if stats else None
     d = ring_desc(q, k, n_pos=n_pos, first_pos=first_pos, layout=layout, causal=causal, scale=scale,
                   emulate_copy=emulate_copy, n_streams=n_streams, separate_merge=separate_merge,
-                  visit_order=visit_order, stats=st)
+                  kv_splits=kv_splits, visit_order=visit_order, stats=st)
     need = ra_ring_workspace_size(d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

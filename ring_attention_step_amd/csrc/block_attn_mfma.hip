@@ -154,17 +154,27 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     const int half = lane >> 5;
 
     const int n_qt = (a.q_len + kMq - 1) / kMq;
-    const int64_t n_wg = static_cast<int64_t>(n_qt) * a.Hq * a.B;
+    const int64_t n_wg = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
+    // (64-bit divisions expand to vector code: the results are made scalar
+    // again, as the copy addresses need wave-uniform bases)
     int64_t L = xcd_remap(blockIdx.x, n_wg);
-    const int qt_rank = static_cast<int>(L % n_qt);
+    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.n_splits));
+    L /= a.n_splits;
+    const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % n_qt));
     L /= n_qt;
-    const int h = static_cast<int>(L % a.Hq);
-    const int b = static_cast<int>(L / a.Hq);
+    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.Hq));
+    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / a.Hq));
     const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
     const int hk = h / (a.Hq / a.Hkv);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1];
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1];
+    // A key split sees keys [k_lo, k_lo + kv_len) of the block as a block of
+    // its own: key c' of the split is key k_lo + c', so its mask offset is
+    // mask_offset - k_lo.
+    const int k_lo = split * a.split_tiles * kNk;
+    const int kv_len = a.n_splits > 1 ? max(0, min(a.kv_len - k_lo, a.split_tiles * kNk)) : a.kv_len;
+    const int mask_offset = a.mask_offset - k_lo;
+    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1] + k_lo * a.ks[2];
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1] + k_lo * a.vs[2];
 
     const int r0 = qt * kMq;
     const int q0w = r0 + wave * 32;  // first query row of this wave
@@ -180,18 +190,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
             qreg[kb] = bf16x8{};
     }
 
-    int key_end = a.kv_len;
-    if (a.causal) key_end = min(key_end, min(a.q_len - 1, r0 + kMq - 1) + a.mask_offset + 1);
+    int key_end = kv_len;
+    if (a.causal) key_end = min(key_end, min(a.q_len - 1, r0 + kMq - 1) + mask_offset + 1);
     const int n_tiles = key_end > 0 ? (key_end + kNk - 1) / kNk : 0;
 
     // keys this wave may see, and keys every row of this wave sees
     int wave_key_end = 0, wave_full_end = 0;
     if (q0w < a.q_len) {
-        wave_key_end = a.kv_len;
-        wave_full_end = a.kv_len;
+        wave_key_end = kv_len;
+        wave_full_end = kv_len;
         if (a.causal) {
-            wave_key_end = min(a.kv_len, min(a.q_len - 1, q0w + 31) + a.mask_offset + 1);
-            wave_full_end = max(0, min(a.kv_len, q0w + a.mask_offset + 1));
+            wave_key_end = min(kv_len, min(a.q_len - 1, q0w + 31) + mask_offset + 1);
+            wave_full_end = max(0, min(kv_len, q0w + mask_offset + 1));
         }
     }
 
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
                           __attribute__((always_inline)) {
         const uint16_t* base = src + static_cast<int64_t>(t) * kNk * stride;
         const uint32_t dst = lds0 + buf * TILE_BYTES;
-        const int last = a.kv_len - 1 - t * kNk;  // last valid row of this tile
+        const int last = kv_len - 1 - t * kNk;  // last valid row of this tile
         if (last >= kNk - 1) {
 #pragma unroll
             for (int i = 0; i < PER_WAVE; ++i) lds_dma16(base, off[i], dst + (wave * PER_WAVE + i) * 1024);
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                    const bool vis = key < a.kv_len && (!a.causal || key <= row + a.mask_offset);
+                    const bool vis = key < kv_len && (!a.causal || key <= row + mask_offset);
                     sacc[sub][v] = vis ? sacc[sub][v] : -INFINITY;
                 }
             }
@@ -409,7 +419,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         const int64_t stride = gk ? ks2 : vs2;
         const uint16_t* src = (gk ? kp : vp) + static_cast<int64_t>(tc) * kNk * stride;
         const uint32_t stride2 = static_cast<uint32_t>(stride * 2);
-        const int last = a.kv_len - 1 - tc * kNk;  // last row of the block within tile tc
+        const int last = kv_len - 1 - tc * kNk;  // last row of the block within tile tc
         const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
         if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
         mfma_stream.template operator()<true, true>(t - 1, t, [&](int n) __attribute__((always_inline)) {
@@ -483,13 +493,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     const float l_ref = xhalf_sum(l_run);
     if (row < a.q_len) {
         const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + row;
-        float* orow = a.o + idx * D;
+        float* const mrow = a.m + split * a.part_ml_stride;
+        float* const lrow = a.l + split * a.part_ml_stride;
+        float* orow = a.o + split * a.part_o_stride + idx * D;
         float m_out = m_true;  // log2 units
         float wa = 0.f, l_a = 0.f;
         float wp = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
         if (a.accumulate) {
-            const float m_a = a.m[idx] * kLog2e;  // -inf stays -inf
-            l_a = a.l[idx];
+            const float m_a = mrow[idx] * kLog2e;  // -inf stays -inf
+            l_a = lrow[idx];
             m_out = fmaxf(m_a, m_true);
             wa = (m_a == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_a - m_out);
             wp = (m_true == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_out);
@@ -510,8 +522,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
             }
         }
         if (half == 0) {
-            a.m[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
-            a.l[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
+            mrow[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
+            lrow[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
         }
     }
 }
@@ -530,11 +542,15 @@ bool mfma_eligible(const BlockArgs& a, int dtype) {
     return true;
 }
 
+int mfma_key_tile() { return kNk; }
+int mfma_query_tile() { return 32 * kWaves; }
+
 hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s) {
     if (a.q_len == 0) return hipSuccess;
     constexpr int kMq = 32 * kWaves;
     const int n_qt = (a.q_len + kMq - 1) / kMq;
-    const int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B;
+    if (a.n_splits < 1 || (a.n_splits > 1 && (a.accumulate || a.split_tiles < 1))) return hipErrorInvalidValue;
+    const int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
     if (a.D == 128)
         hipLaunchKernelGGL((block_mfma_kernel<128, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
                            0, s, a);

@@ -8,6 +8,9 @@
 //     l = w_a l_a + w_p l_p,  o = w_a o_a + w_p o_p,
 // and finalisation gives o / l (0 when l = 0) and lse = m + ln l.
 //
+// Several partials (the key splits of one block) can fold in one pass, and
+// the running state may be declared empty (a position's first step).
+//
 // HBM-bound streaming kernel.  All lanes that handle one row sit in the same
 // wavefront, and every lane reads the row's (m, l) before any lane of the
 // wavefront writes them back, so the in-place update of (m_acc, l_acc) is
@@ -23,7 +26,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-template <int VEC>
+// MAXP bounds the partials one launch folds; a two-way merge compiles with
+// MAXP = 1 so it keeps the register budget of a plain streaming kernel.
+template <int VEC, int MAXP>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a, int tpr) {
     const int lane = threadIdx.x & 63;
     const int rows_per_wave = 64 / tpr;
@@ -32,15 +37,26 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a, int t
     const int g = lane % tpr;
     if (row >= a.rows) return;
 
-    const float ma = a.m_acc[row], la = a.l_acc[row];
-    float m = ma, wa = 1.f, wp = 0.f, l = la;
+    // running state (or empty) and the partials' weights w_x = exp(m_x - m)
+    const float ma = a.acc_valid ? a.m_acc[row] : -INFINITY;
+    const float la = a.acc_valid ? a.l_acc[row] : 0.f;
     const bool fold = a.o_p != nullptr;
-    if (fold) {
-        const float mp = a.m_p[row], lp = a.l_p[row];
-        m = fmaxf(ma, mp);
-        wa = (ma == -INFINITY) ? 0.f : expf(ma - m);
-        wp = (mp == -INFINITY) ? 0.f : expf(mp - m);
-        l = wa * la + wp * lp;
+    const int np = fold ? a.n_parts : 0;
+    float m = ma;
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i)
+        if (i < np) m = fmaxf(m, a.m_p[i * a.part_ml_stride + row]);
+    const float wa = (ma == -INFINITY) ? 0.f : expf(ma - m);
+    float l = wa * la;
+    float wp[MAXP];
+#pragma unroll
+    for (int i = 0; i < MAXP; ++i) {
+        wp[i] = 0.f;
+        if (i < np) {
+            const float mp = a.m_p[i * a.part_ml_stride + row];
+            wp[i] = (mp == -INFINITY) ? 0.f : expf(mp - m);
+            l += wp[i] * a.l_p[i * a.part_ml_stride + row];
+        }
     }
     const bool finalize = a.o_out != nullptr || a.lse_out != nullptr;
     const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -48,16 +64,18 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeArgs a, int t
     for (int c = g * VEC; c < a.D; c += tpr * VEC) {
         float o[VEC];
         if (VEC == 4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(a.o_acc + base + c);
-            o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
-            if (fold) {
-                const f32x4 y = *reinterpret_cast<const f32x4*>(a.o_p + base + c);
+            f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (a.acc_valid) x = *reinterpret_cast<const f32x4*>(a.o_acc + base + c) * (fold ? wa : 1.f);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = wa * o[e] + wp * y[e];
-            }
+            for (int i = 0; i < MAXP; ++i)
+                if (i < np) x += wp[i] * *reinterpret_cast<const f32x4*>(a.o_p + i * a.part_o_stride + base + c);
+            o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
         } else {
-            o[0] = a.o_acc[base + c];
-            if (fold) o[0] = wa * o[0] + wp * a.o_p[base + c];
+            float x = a.acc_valid ? a.o_acc[base + c] * (fold ? wa : 1.f) : 0.f;
+#pragma unroll
+            for (int i = 0; i < MAXP; ++i)
+                if (i < np) x += wp[i] * a.o_p[i * a.part_o_stride + base + c];
+            o[0] = x;
         }
         if (finalize) {
             if (a.o_out != nullptr) {
@@ -104,16 +122,23 @@ bool aligned(const void* p, uintptr_t n) { return p == nullptr || (reinterpret_c
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
     if (a.rows == 0) return hipSuccess;
     const bool vec = (a.D % 4 == 0) && aligned(a.o_acc, 16) && aligned(a.o_p, 16) &&
-                     aligned(a.o_out, a.out_dtype == 1 ? 8 : 16);
+                     aligned(a.o_out, a.out_dtype == 1 ? 8 : 16) && (a.part_o_stride % 4 == 0);
     const int units = vec ? a.D / 4 : a.D;
     int tpr = 1;
     while (tpr < units && tpr < 64) tpr <<= 1;
     const int64_t rows_per_block = 256 / tpr;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
-    if (vec)
-        hipLaunchKernelGGL(lse_merge_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, tpr);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    const bool multi = a.o_p != nullptr && a.n_parts > 1;
+    if (a.o_p != nullptr && (a.n_parts < 1 || a.n_parts > kMaxMergeParts)) return hipErrorInvalidValue;
+    if (vec && multi)
+        hipLaunchKernelGGL((lse_merge_kernel<4, kMaxMergeParts>), grid, dim3(256), 0, s, a, tpr);
+    else if (vec)
+        hipLaunchKernelGGL((lse_merge_kernel<4, 1>), grid, dim3(256), 0, s, a, tpr);
+    else if (multi)
+        hipLaunchKernelGGL((lse_merge_kernel<1, kMaxMergeParts>), grid, dim3(256), 0, s, a, tpr);
     else
-        hipLaunchKernelGGL(lse_merge_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, tpr);
+        hipLaunchKernelGGL((lse_merge_kernel<1, 1>), grid, dim3(256), 0, s, a, tpr);
     return hipGetLastError();
 }
 

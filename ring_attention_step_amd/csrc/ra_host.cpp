@@ -60,6 +60,7 @@ bool valid_dtype(int32_t d) { return d == RA_F32 || d == RA_BF16; }
 bool aligned_to(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int64_t kMaxLen = (int64_t(1) << 31) - 1;
+constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
 
 // Shared shape checks of the block and ring descriptors.
 ra_status check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
@@ -83,6 +84,8 @@ ra_status launch_block(const ra::BlockArgs& a, int32_t dtype, uint32_t flags, hi
     hipError_t e;
     if (!(flags & RA_BLOCK_FORCE_SIMT) && ra::mfma_eligible(a, dtype))
         e = ra::launch_block_mfma(a, s);
+    else if (a.n_splits > 1)
+        return fail(RA_ERR_UNSUPPORTED, "key splits need the MFMA kernel");
     else
         e = ra::launch_block_simt(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "block attention launch");
@@ -226,6 +229,8 @@ struct RingGeometry {
     int64_t q_elems;    // B * Hq * Sb * D   (one position's query shard / output)
     int64_t kv_elems;   // B * Hkv * Sb * D  (one key or value shard)
     int32_t n_streams;
+    int32_t n_splits, split_tiles;  // key splits of every block launch (1: none)
+    int32_t n_part;                 // partials per stream (0, 1 or n_splits)
     size_t acc_o, acc_ml, part_o, part_ml, slot;  // bytes, each 256-aligned
     size_t total;
 };
@@ -243,6 +248,8 @@ ra_status check_ring(const ra_ring_desc* d) {
     if (d->emulate_copy != 0 && d->emulate_copy != 1) return fail(RA_ERR_INVALID, "emulate_copy must be 0 or 1");
     if (d->n_streams < 0 || d->n_streams > 64) return fail(RA_ERR_INVALID, "n_streams must be in [0, 64]");
     if (d->separate_merge != 0 && d->separate_merge != 1) return fail(RA_ERR_INVALID, "separate_merge must be 0 or 1");
+    if (d->kv_splits < 0 || d->kv_splits > ra::kMaxMergeParts)
+        return fail(RA_ERR_INVALID, "kv_splits must be in [0, %d]", ra::kMaxMergeParts);
     if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
     if (d->visit_order) {
         std::vector<char> seen(d->n_pos, 0);
@@ -264,12 +271,34 @@ RingGeometry geometry(const ra_ring_desc* d) {
     g.n_streams = d->n_streams > 0 ? std::min(d->n_streams, d->n_run) : std::min(d->n_run, 8);
     g.acc_o = round_up(static_cast<size_t>(g.q_elems) * 4, 256);
     g.acc_ml = round_up(static_cast<size_t>(g.rows) * 4, 256);
-    g.part_o = d->separate_merge ? g.acc_o : 0;  // per-stream partials only for the separate schedule
-    g.part_ml = d->separate_merge ? g.acc_ml : 0;
+    // Key splits (fused schedule, MFMA shapes): when one step's block launches
+    // fill few workgroups, each launch cuts the keys into n_splits ranges of
+    // split_tiles tiles, one workgroup per (query tile, head, range), and a
+    // multi-partial ra_lse_merge pass folds the ranges into the running state.
+    g.n_splits = 1;
+    g.split_tiles = 0;
+    if (!d->separate_merge && d->kv_splits != 1 && d->dtype == RA_BF16 &&
+        (d->head_dim == 64 || d->head_dim == 128)) {
+        const int64_t tiles = (Sb + ra::mfma_key_tile() - 1) / ra::mfma_key_tile();
+        int64_t want = d->kv_splits;
+        if (want == 0) {  // automatic: about one workgroup per compute unit, >= 2 key tiles per range
+            const int64_t wg = (Sb + ra::mfma_query_tile() - 1) / ra::mfma_query_tile() * d->q_heads * d->batch *
+                               std::min(g.n_streams, d->n_run);
+            want = wg >= kCUs ? 1 : std::min<int64_t>((kCUs + wg - 1) / wg, tiles / 2);
+        }
+        want = std::max<int64_t>(1, std::min<int64_t>({want, tiles, ra::kMaxMergeParts}));
+        if (want > 1) {
+            g.split_tiles = static_cast<int32_t>((tiles + want - 1) / want);
+            g.n_splits = static_cast<int32_t>((tiles + g.split_tiles - 1) / g.split_tiles);  // no empty range
+        }
+    }
+    g.n_part = d->separate_merge ? 1 : (g.n_splits > 1 ? g.n_splits : 0);
+    g.part_o = g.n_part ? g.acc_o : 0;
+    g.part_ml = g.n_part ? g.acc_ml : 0;
     g.slot = d->emulate_copy ? round_up(static_cast<size_t>(g.kv_elems) * elem_size(d->dtype), 256) : 0;
-    // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: partial o, m, l
+    // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: n_part partials o, m, l
     g.total = static_cast<size_t>(d->n_run) * (g.acc_o + 2 * g.acc_ml + 4 * g.slot) +
-              static_cast<size_t>(g.n_streams) * (g.part_o + 2 * g.part_ml);
+              static_cast<size_t>(g.n_streams) * g.n_part * (g.part_o + 2 * g.part_ml);
     return g;
 }
 
@@ -390,14 +419,14 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     struct StreamBufs {
         float *o, *m, *l;
     };
-    std::vector<StreamBufs> part(g.n_streams);
+    std::vector<StreamBufs> part(g.n_streams);  // partial i at o + i part_o, m / l + i part_ml
     for (int s = 0; s < g.n_streams; ++s) {
         part[s].o = reinterpret_cast<float*>(ws);
-        ws += g.part_o;
+        ws += g.n_part * g.part_o;
         part[s].m = reinterpret_cast<float*>(ws);
-        ws += g.part_ml;
+        ws += g.n_part * g.part_ml;
         part[s].l = reinterpret_cast<float*>(ws);
-        ws += g.part_ml;
+        ws += g.n_part * g.part_ml;
     }
 
     std::vector<std::vector<RingPlanStep>> plan(d->n_run);
@@ -416,6 +445,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         }
     }
     stats.flops = 4.0 * D * stats.unmasked_pairs;
+    stats.kv_splits = 1;
 
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
@@ -513,6 +543,18 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                 a.scale = resolve_scale(d->scale, D);
                 a.causal = d->causal;
                 a.mask_offset = clamp_offset(ps.offset, Sb, Sb);
+                const bool split = g.n_splits > 1 && ra::mfma_eligible(a, d->dtype);
+                if (split) {  // the block's key ranges as partials, folded by the merge below
+                    stats.kv_splits = g.n_splits;
+                    a.o = part[sid].o;
+                    a.m = part[sid].m;
+                    a.l = part[sid].l;
+                    a.accumulate = 0;
+                    a.n_splits = g.n_splits;
+                    a.split_tiles = g.split_tiles;
+                    a.part_o_stride = static_cast<int64_t>(g.part_o / 4);
+                    a.part_ml_stride = static_cast<int64_t>(g.part_ml / 4);
+                }
                 size_t t0 = 0;
                 st = timer.begin(cs, t0);
                 if (st != RA_OK) return st;
@@ -524,17 +566,23 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                     RA_HIP(hipEventRecord(ev_used(p, par), cs));
                     used_parity[2 * p + par] = 1;
                 }
-                if ((!first && !fused) || last) {
+                if ((!first && !fused) || last || split) {
                     ra::MergeArgs ma{};
                     ma.rows = g.rows;
                     ma.D = D;
                     ma.o_acc = pos[p].o;
                     ma.m_acc = pos[p].m;
                     ma.l_acc = pos[p].l;
-                    if (!first && !fused) {
+                    if ((!first && !fused) || split) {
                         ma.o_p = part[sid].o;
                         ma.m_p = part[sid].m;
                         ma.l_p = part[sid].l;
+                    }
+                    if (split) {
+                        ma.n_parts = g.n_splits;
+                        ma.part_o_stride = static_cast<int64_t>(g.part_o / 4);
+                        ma.part_ml_stride = static_cast<int64_t>(g.part_ml / 4);
+                        ma.acc_valid = first ? 0 : 1;
                     }
                     if (last) {
                         ma.o_out = obase + static_cast<size_t>(p) * g.q_elems * es;

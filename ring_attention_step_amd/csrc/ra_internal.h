@@ -27,6 +27,12 @@ struct BlockArgs {
     int32_t mask_offset;  // key c visible to row r iff c <= r + mask_offset
     int32_t accumulate;   // 0: write the block's partial to (o, m, l);
                           // 1: (o, m, l) hold a running state; merge the partial into it
+    // Key split (MFMA kernel only): n_splits > 1 cuts the block's keys into
+    // ranges of split_tiles key tiles; split i writes its own partial to
+    // o + i part_o_stride, m / l + i part_ml_stride (accumulate must be 0).
+    int32_t n_splits = 1;
+    int32_t split_tiles = 0;
+    int64_t part_o_stride = 0, part_ml_stride = 0;
 };
 
 // Vector-ALU kernel: binary32 or bfloat16 inputs, any D in [1, 256], fp32 math.
@@ -34,6 +40,8 @@ hipError_t launch_block_simt(const BlockArgs& a, int dtype, hipStream_t s);
 
 // bf16 MFMA kernel (gfx950): D in {64, 128}; 16-byte aligned rows.
 bool mfma_eligible(const BlockArgs& a, int dtype);
+int mfma_key_tile();    // keys per LDS tile of the MFMA kernel
+int mfma_query_tile();  // query rows per workgroup of the MFMA kernel
 hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s);
 
 // Backward of one query block against one key/value block: this pair's share
@@ -85,7 +93,14 @@ struct MergeArgs {
     void* o_out;  // finalise when o_out or lse_out is non-NULL
     int32_t out_dtype;
     float* lse_out;
+    // Several partials (o_p + i part_o_stride, ... for i < n_parts, at most
+    // kMaxMergeParts) fold in one pass; acc_valid = 0 treats the running state
+    // as empty (it is not read) -- the first step of a split-key position.
+    int32_t n_parts = 1;
+    int32_t acc_valid = 1;
+    int64_t part_o_stride = 0, part_ml_stride = 0;
 };
+constexpr int kMaxMergeParts = 8;
 hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 
 // Row moves between [BH, S, row] and [N, BH, S/N, row] under a token map.

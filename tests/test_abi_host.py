@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     for name in names:
         assert hasattr(lib, name), f"libra.so does not export {name}"
     assert set(names) == set(B.EXPORTS)
-    assert lib.ra_abi_version() == 3
+    assert lib.ra_abi_version() == 4
 
 
 def test_mask_offset_is_floor_division(lib):
@@ -171,7 +171,8 @@ def test_ring_workspace_and_validation(lib):
     assert lib.ra_ring_workspace_size(ctypes.byref(e), ctypes.byref(n)) == B.RA_OK
     assert n.value == (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2)
     for kw in ({"first_pos": 32}, {"n_run": 2}, {"layout": 3}, {"n_pos": 0}, {"block_len": 0},
-               {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}, {"separate_merge": 2}):
+               {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}, {"separate_merge": 2},
+               {"kv_splits": -1}, {"kv_splits": 9}):
         bad = _ring_desc(**kw)
         assert lib.ra_ring_workspace_size(ctypes.byref(bad), ctypes.byref(n)) != B.RA_OK
     order = (ctypes.c_int32 * 32)(*([0] * 32))
@@ -181,6 +182,36 @@ def test_ring_workspace_and_validation(lib):
     # too small a workspace is refused before anything runs
     st = lib.ra_ring_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, ctypes.c_void_p(0x100000), 1024, None)
     assert st == B.RA_ERR_WORKSPACE
+
+
+def test_kv_split_workspace(lib):
+    """Key splits: a ring whose block launches fill few workgroups keeps
+    n_splits partials per stream (one per 128-key range); 0 chooses the count
+    so that the launches of one step reach about 256 workgroups."""
+    n = ctypes.c_size_t()
+    # 2 positions of 2048 tokens, 4 heads, d 64: 8 query tiles x 4 heads x 2 streams = 64 workgroups
+    kw = dict(q_heads=4, kv_heads=4, head_dim=64, n_pos=2, first_pos=0, n_run=2, block_len=2048, causal=0,
+              layout=B.RA_CONTIGUOUS)
+    rows = 4 * 2048
+    state = rows * 64 * 4 + 2 * rows * 4  # fp32 O, m, l of one position (all 256-byte multiples)
+
+    def size(**extra):
+        d = _ring_desc(**kw, **extra)
+        assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
+        return n.value
+
+    assert size(kv_splits=1) == 2 * state
+    assert size() == 2 * state + 2 * 4 * state  # automatic: 4 ranges of 4 tiles
+    assert size(kv_splits=8) == 2 * state + 2 * 8 * state
+    assert size(kv_splits=3) == 2 * state + 2 * 3 * state  # 6 + 6 + 4 tiles
+    assert size(kv_splits=5) == 2 * state + 2 * 4 * state  # 4-tile ranges: the fifth would be empty
+    assert size(separate_merge=1) == 2 * state + 2 * state  # one partial per stream, no splits
+    assert size(n_streams=1) == 2 * state + 1 * 8 * state  # 32 workgroups per step: 8 ranges of 2 tiles
+    assert size(dtype=B.RA_F32) == 2 * state  # the vector-ALU kernel has no key splits
+    kw["block_len"] = 128  # one key tile: nothing to split
+    rows = 4 * 128
+    state = rows * 64 * 4 + 2 * rows * 4
+    assert size() == 2 * state and size(kv_splits=4) == 2 * state
 
 
 def test_backward_validation(lib):

@@ -190,10 +190,17 @@ def test_config2_noncausal_bf16_all_rows():
     gh.say("ra_ring_forward config2")
     qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16")
     qs, ks, vs = (gh.shards_on_device(x, N, "contiguous", "bf16") for x in (qn, kn, vn))
-    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", False, stats=True)
-    assert st["block_launches"] == 4 and st["merge_launches"] == 2 and st["blocks_skipped"] == 0  # 1 finalise each
-    assert st["flops"] == 4 * D * H * S * S
     hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    # 8 query tiles x 4 heads per launch: the automatic schedule splits each
+    # block's keys into 4 ranges and folds them with one merge pass per step
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", False, stats=True)
+    assert st["block_launches"] == 4 and st["merge_launches"] == 4 and st["blocks_skipped"] == 0
+    assert st["kv_splits"] == 4
+    assert st["flops"] == 4 * D * H * S * S
+    gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "contiguous", 0, False, "bf16")
+    # without splits: the merge is fused into the block kernel, one finalise per position
+    o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "contiguous", False, kv_splits=1, stats=True)
+    assert st["block_launches"] == 4 and st["merge_launches"] == 2
     gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, "contiguous", 0, False, "bf16")
 
 
@@ -344,7 +351,7 @@ def test_fused_and_separate_merge_rings_agree(lay, causal):
     gh.say("ra_ring_forward fused vs separate", lay, causal)
     N, S, H = 4, 2048, 4
     (qn, kn, vn), (qs, ks, vs) = _small_ring_inputs(S=S, H=H, N=N, lay=lay)
-    o1, l1, st1 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, stats=True)
+    o1, l1, st1 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, kv_splits=1, stats=True)
     o2, l2, st2 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, separate_merge=True, stats=True)
     # fused: one finalising pass per position; separate: one fold per block after the
     # first (the last one also finalises), and one pass where a position has a single block
@@ -356,3 +363,80 @@ def test_fused_and_separate_merge_rings_agree(lay, causal):
     hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
     for o, lse in ((o1, l1), (o2, l2)):
         gh.compare_rows(o, lse, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, causal, "bf16")
+
+
+@pytest.mark.parametrize("lay,causal,D,Sb,N,splits,used", [
+    ("contiguous", True, 128, 1000, 2, 3, 3),  # ragged last range; diagonal block: early tiles see empty ranges
+    ("contiguous", True, 64, 640, 3, 0, 2),    # automatic count over 5 tiles: 2 ranges of 3 and 2 tiles
+    ("striped", True, 128, 1000, 2, 8, 8),     # 8 ranges of one tile
+    ("striped", False, 64, 384, 4, 2, 2),
+    ("striped", False, 64, 384, 4, 8, 3),      # capped at the block's 3 tiles
+    ("contiguous", False, 128, 2048, 2, 8, 8),
+])
+def test_kv_split_ring_matches_oracle(lay, causal, D, Sb, N, splits, used):
+    """Key-split schedule: each block's keys in ranges of whole 128-key tiles,
+    one partial per range, folded by one multi-partial merge per step; every
+    row against the oracle, and close to the unsplit schedule."""
+    H = 2
+    S = Sb * N
+    gh.say("ra_ring_forward kv splits", lay, causal, D, Sb, N, splits)
+    (qn, kn, vn), (qs, ks, vs) = _small_ring_inputs(S=S, H=H, Hkv=1, D=D, N=N, lay=lay, seed=5)
+    o1, l1, st1 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, kv_splits=splits, stats=True)
+    o2, l2, st2 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, kv_splits=1, stats=True)
+    assert st1["kv_splits"] == used and st2["kv_splits"] == 1
+    computed = st1["block_launches"]
+    assert computed == st2["block_launches"] == N * N - st1["blocks_skipped"]
+    assert st1["merge_launches"] == computed  # one fold per computed block, the last also finalises
+    assert st2["merge_launches"] == N
+    assert torch.max(torch.abs(o1.float() - o2.float())) <= 1e-2
+    assert torch.max(torch.abs(l1 - l2)) <= 1e-4
+    hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    gh.compare_rows(o1, l1, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, causal, "bf16")
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_ring_forward_graph_replay(splits):
+    """A whole ring step (permute in, ra_ring_forward, permute out) captured
+    into a HIP graph: every replay, with eager work and synchronisations
+    between replays, reproduces the eager step bit for bit."""
+    B, H, S, D, N = 1, 4, 4096, 64, 2
+    gh.say("ra_ring_forward graph replay", splits)
+    qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16", seed=3)
+    q_g, k_g, v_g = (gh.to_device(x, "bf16") for x in (qn, kn, vn))
+    q_sh = torch.empty((N, B, H, S // N, D), dtype=torch.bfloat16, device="cuda")
+    k_sh, v_sh, o_sh = torch.empty_like(q_sh), torch.empty_like(q_sh), torch.empty_like(q_sh)
+    lse = torch.empty(q_sh.shape[:4], dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q_g)
+    ws = torch.empty(ra.ra_ring_workspace_size(ra.ring_desc(q_sh, k_sh, n_pos=N, kv_splits=splits)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        for src, dst in ((q_g, q_sh), (k_g, k_sh), (v_g, v_sh)):
+            ra.ra_stripe_permute(src, dst, layout="contiguous", inverse=False, n_pos=N)
+        ra.ra_ring_forward(q_sh, k_sh, v_sh, o_sh, lse, n_pos=N, workspace=ws, kv_splits=splits)
+        ra.ra_stripe_permute(o_sh, out, layout="contiguous", inverse=True, n_pos=N)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l)
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o)
+    hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
+    sel = np.arange(0, H * S, 37)
+    gh.compare_rows(o_sh, lse, qn, kn, vn, hh.ravel()[sel], tt.ravel()[sel], N, "contiguous", 0, False, "bf16")
