@@ -293,3 +293,36 @@ def test_batch2_gqa4_ring_forward_and_backward(lay):
     want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
     for name, got, ref in zip(("dq", "dk", "dv"), grads, want):
         _close(gh.to_host_f64(got), ref, 2e-2, name)
+
+
+@pytest.mark.timeout(900)
+def test_backward_identical_keys_closed_form_at_scale():
+    """Every key of a head equal (k_c = k0) over the 256K-token striped ring:
+    the causal softmax of row t is uniform, p_tc = 1 / (t + 1) for c <= t, so
+        dV_c = sum over t >= c of dO_t / (t + 1)     (every key, all heads),
+    and dS_tc = p_tc dO_t . (v_c - O_t) sums to zero over c, so dQ_t = 0 up to
+    rounding (every row).  The reference is a float64 suffix sum on the host."""
+    B, H, S, D, N = 1, 8, 262144, 128, 8
+    gh.say("ra_ring_backward identical keys 256k")
+    qn = ra_inputs.normal((B, H, S, D), ra_inputs.STREAM_Q, seed=29, dtype="bf16")
+    k0 = ra_inputs.normal((B, H, 1, D), ra_inputs.STREAM_K, seed=29, dtype="bf16")
+    vn = ra_inputs.normal((B, H, S, D), ra_inputs.STREAM_V, seed=29, dtype="bf16")
+    gn = ra_inputs.normal((B, H, S, D), 3, seed=29, dtype="bf16")
+    kn = np.broadcast_to(k0, (B, H, S, D))
+    qs, ks, vs, gs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (qn, kn, vn, gn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, "striped", True)
+    dq = torch.empty(qs.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    ra.ra_ring_backward(qs, ks, vs, o, gs, lse, dq, dk, dv, n_pos=N, layout="striped", causal=True)
+    full = {}
+    for name, sh in (("dq", dq), ("dv", dv)):
+        full[name] = torch.empty(B, H, S, D, device="cuda")
+        ra.ra_stripe_permute(sh, full[name], layout="striped", inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    inv = 1.0 / np.arange(1, S + 1, dtype=np.float64)
+    for h in range(H):
+        g = ra_inputs.bf16_to_f32(gn[0, h]).astype(np.float64) * inv[:, None]
+        want_dv = np.cumsum(g[::-1], axis=0)[::-1]
+        _close(gh.to_host_f64(full["dv"][0, h]), want_dv, 2e-2, f"dv head {h}")
+        _close(gh.to_host_f64(full["dq"][0, h]), np.zeros((S, D)), 2e-2, f"dq head {h}")

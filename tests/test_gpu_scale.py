@@ -94,3 +94,41 @@ def test_dominant_self_key_at_scale():
     torch.cuda.synchronize()
     dev = np.max(np.abs(gh.to_host_f64(full2)[0][:, 1:-1] - v_f[:, 2:]), axis=-1)
     assert np.min(dev) > 0.1  # no row collapsed onto its (masked) future key
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("lay", ["striped", "contiguous"])
+def test_identical_keys_closed_form_at_scale(lay):
+    """Every key of a head equal (k_c = k0): all visible scores of row t are the
+    same, so the causal softmax is uniform over the t + 1 keys it may see and,
+    for every one of the 2M rows at the 256K-token shape,
+        O_t = mean(v_0 .. v_t),   lse_t = scale * (q_t . k0) + ln(t + 1).
+    The count t + 1 pins the diagonal and the layout's mask at every row; the
+    reference is a float64 prefix mean on the host."""
+    B, H, S, D, N = 1, 8, 262144, 128, 8
+    gh.say("ra_ring_forward identical keys", lay)
+    qn = ra_inputs.normal((B, H, S, D), ra_inputs.STREAM_Q, seed=23, dtype="bf16")
+    k0 = ra_inputs.normal((B, H, 1, D), ra_inputs.STREAM_K, seed=23, dtype="bf16")
+    vn = ra_inputs.normal((B, H, S, D), ra_inputs.STREAM_V, seed=23, dtype="bf16")
+    kn = np.broadcast_to(k0, (B, H, S, D))
+    qs, ks, vs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
+    full = torch.empty(B, H, S, D, device="cuda", dtype=torch.bfloat16)
+    ra.ra_stripe_permute(o, full, layout=lay, inverse=True, n_pos=N)
+    lse_full = torch.empty(B, H, S, 1, device="cuda")
+    ra.ra_stripe_permute(lse[..., None].contiguous(), lse_full, layout=lay, inverse=True, n_pos=N)
+    torch.cuda.synchronize()
+    count = np.arange(1, S + 1, dtype=np.float64)
+    scale = 1.0 / np.sqrt(D)
+    for h in range(H):
+        v = ra_inputs.bf16_to_f32(vn[0, h]).astype(np.float64)
+        want_o = np.cumsum(v, axis=0) / count[:, None]
+        got_o = gh.to_host_f64(full[0, h])
+        err_o = float(np.max(np.abs(got_o - want_o)))
+        assert err_o <= gh.TOL["bf16"]["o"], (h, err_o)
+        s = (ra_inputs.bf16_to_f32(qn[0, h]).astype(np.float64) @
+             ra_inputs.bf16_to_f32(k0[0, h, 0]).astype(np.float64)) * scale
+        err_l = np.abs(gh.to_host_f64(lse_full[0, h, :, 0]) - (s + np.log(count)))
+        # fp32 scores and an exact count: far inside the 1e-3 bound, and tight enough that
+        # a count off by one is visible on every row t < 2e4
+        assert float(np.max(err_l)) <= 5e-5, (h, float(np.max(err_l)), int(np.argmax(err_l)))
