@@ -34,6 +34,7 @@
 // the other's vector work (eight-wave workgroups sharing each tile measured
 // slower).
 #include <cmath>
+#include <type_traits>
 
 #include "mfma_common.h"
 #include "ra_internal.h"
@@ -169,6 +170,9 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
         greg[kb] = row_ok ? *reinterpret_cast<const bf16x8*>(gp + row * a.dos[2] + kb * 16 + half * 8) : bf16x8{};
     }
     const float lse2 = row_ok ? a.lse[row0 + row] * kLog2e : -INFINITY;
+    // exp2 argument offset: -lse (log2 units), or -inf for a row that sees no
+    // key at all (and for rows past the block), which makes every p exactly 0
+    const float nl2 = lse2 == -INFINITY ? -INFINITY : -lse2;
     const float dlt = row_ok ? a.delta[row0 + row] : 0.f;
     const float c2 = a.scale * kLog2e;
 
@@ -220,18 +224,29 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
                 dp[sub] = MFMA(rd.rows(vt, sub, kb), greg[kb], dp[sub]);
             }
         }
-        const bool edge = kbase + kTile > wave_full_end;  // diagonal or ragged tile
+        // Mask (diagonal / ragged tiles only): masked scores become -inf, so
+        // that their exp2 below is exactly 0 (the scale is positive).
+        // Register v of sub-tile sub holds key kbase + 4 half + j, with the
+        // compile-time j = 32 sub + 8 (v/4) + v%4: visible iff
+        // j < kv_len - kbase - 4 half and (causal) j <= row + mask_offset - kbase - 4 half.
+        if (kbase + kTile > wave_full_end) {
+            const int k_lim = a.kv_len - kbase - 4 * half;
+            const int c_lim = a.causal ? row + a.mask_offset - kbase - 4 * half : k_lim;
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int j = sub * 32 + 8 * (v / 4) + (v % 4);
+                    s[sub][v] = ((j < k_lim) & (j <= c_lim)) ? s[sub][v] : -INFINITY;
+                }
+        }
+        // dS^T = P^T (dP^T - delta)
         bf16x8 dsr[2 * SUB];
 #pragma unroll
         for (int sub = 0; sub < SUB; ++sub) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                bool vis = lse2 != -INFINITY;
-                if (edge) vis = vis && key < a.kv_len && (!a.causal || key <= row + a.mask_offset);
-                const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], c2, -lse2)) : 0.f;
-                s[sub][v] = p * (dp[sub][v] - dlt);
-            }
+            for (int v = 0; v < 16; ++v)
+                s[sub][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], c2, nl2)) * (dp[sub][v] - dlt);
             dsr[2 * sub] = pack_bf16x8(s[sub], 0);
             dsr[2 * sub + 1] = pack_bf16x8(s[sub], 8);
         }
@@ -359,7 +374,8 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         const lds_char* qt = lds + (st & 1) * BUF;
         const lds_char* gt = qt + TB;
         const float* ls = reinterpret_cast<const float*>(smem + (st & 1) * BUF + 2 * TB);
-        const bool edge = rb < wave_row_full || rb + kTile > a.q_len;
+        // edge tiles: the diagonal, the ragged end of the rows, or keys past the block
+        const bool edge = rb < wave_row_full || rb + kTile > a.q_len || c0w + 32 > a.kv_len;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             // S = Q K^T, then P; P^T (bf16) feeds dV at once so that the fp32
@@ -376,8 +392,10 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
                     const int r = rb + rt + e;
-                    bool vis = key_ok && l4[e] != -INFINITY;
-                    if (edge) vis = vis && r < a.q_len && (!a.causal || key <= r + a.mask_offset);
+                    // off edge tiles every pair is visible (and the row's lse finite:
+                    // a row whose lse is -inf sees no key, so it lies on an edge tile)
+                    bool vis = true;
+                    if (edge) vis = key_ok && l4[e] != -INFINITY && r < a.q_len && (!a.causal || key <= r + a.mask_offset);
                     s[v] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c2, -l4[e])) : 0.f;
                 }
             }
