@@ -33,6 +33,7 @@
 // Two workgroups of four waves share a CU, so one workgroup's MFMAs overlap
 // the other's vector work (eight-wave workgroups sharing each tile measured
 // slower).
+#include <climits>
 #include <cmath>
 #include <type_traits>
 
@@ -117,6 +118,16 @@ struct TileCopy {
     __device__ void init(int wave, int lane) {
         crow0 = wave * PER * RPI + lane / CPR;
         cpos = lane % CPR;
+    }
+    // The same plan with the lane index recomputed at the call (volatile, so
+    // the compiler cannot hoist it and keep crow0 / cpos live through a loop
+    // where registers are short).
+    __device__ static TileCopy here(int wave) {
+        int ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        TileCopy c;
+        c.init(wave, ln);
+        return c;
     }
     // rows [r0, r0 + kTile) of src (row stride in elements); rows past n_rows
     // re-read the last row (finite values, masked later)
@@ -320,8 +331,6 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
 
     TileReads<D> rd;
     rd.init(lane);
-    TileCopy<D, kKvWaves> cp;
-    cp.init(wave, lane);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     const lds_char* lds = RA_LDS_PTR(char, smem);
 
@@ -336,6 +345,7 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         const int h = hk * grp + hi;
         const int rb = row_start + t * kTile;
         const uint32_t buf = lds0 + (st & 1) * BUF;
+        const auto cp = TileCopy<D, kKvWaves>::here(wave);
         cp.issue(static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1], a.qs[2], rb, a.q_len, buf, wave);
         cp.issue(static_cast<const uint16_t*>(a.dout) + b * a.dos[0] + h * a.dos[1], a.dos[2], rb, a.q_len,
                   buf + TB, wave);
@@ -364,6 +374,15 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
     }
     for (int st = 0; st < n_steps; ++st) {
         wait_vmem_all();
+        static_assert(kTile == 64, "one lane per row of the tile");
+        if (wave == 0) {
+            // wave 0 copied the tile's lse; turn it in place into the exp2
+            // offset -lse log2(e), or -inf for a row whose lse is -inf (so that
+            // such a row contributes nothing), before the barrier publishes it
+            float* lsw = reinterpret_cast<float*>(smem + (st & 1) * BUF + 2 * TB);
+            const float l = lsw[lane];
+            lsw[lane] = l == -INFINITY ? -INFINITY : -l * kLog2e;
+        }
         __syncthreads();
         if (st + 1 < n_steps) {
             stats(st + 1);
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         const lds_char* gt = qt + TB;
         const float* ls = reinterpret_cast<const float*>(smem + (st & 1) * BUF + 2 * TB);
         // edge tiles: the diagonal, the ragged end of the rows, or keys past the block
-        const bool edge = rb < wave_row_full || rb + kTile > a.q_len || c0w + 32 > a.kv_len;
+        const bool edge = rb < wave_row_full || rb + kTile > a.q_len;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             // S = Q K^T, then P; P^T (bf16) feeds dV at once so that the fp32
@@ -383,21 +402,30 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
             f32x16 s = f32x16{};
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
-            // rows of register v: 32 qb + 8 (v/4) + 4 half + v%4 within the tile
+            // P; register v holds row rb + 4 half + i of the tile, with the
+            // compile-time i = 32 qb + 8 (v/4) + v%4.  Mask (edge tiles only):
+            // masked scores become -inf, so that their exp2 is exactly 0; a
+            // pair is visible iff i < q_len - rb - 4 half and (causal)
+            // i >= key - mask_offset - rb - 4 half.  Keys past the block need
+            // no mask: each key's dK / dV column is its own and never stored.
+            if (edge) {
+                const int r_lim = a.q_len - rb - 4 * half;
+                const int c_lim = a.causal ? key - a.mask_offset - rb - 4 * half : INT_MIN;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 32 * qb + 8 * g + e;
+                        s[4 * g + e] = ((i < r_lim) & (i >= c_lim)) ? s[4 * g + e] : -INFINITY;
+                    }
+                }
+            }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int rt = 32 * qb + 8 * g + 4 * half;
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + rt) * kLog2e;  // -inf stays -inf
+                const f32x4 nl4 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 8 * g + 4 * half);  // exp2 offsets
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * g + e;
-                    const int r = rb + rt + e;
-                    // off edge tiles every pair is visible (and the row's lse finite:
-                    // a row whose lse is -inf sees no key, so it lies on an edge tile)
-                    bool vis = true;
-                    if (edge) vis = key_ok && l4[e] != -INFINITY && r < a.q_len && (!a.causal || key <= r + a.mask_offset);
-                    s[v] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c2, -l4[e])) : 0.f;
-                }
+                for (int e = 0; e < 4; ++e)
+                    s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c2, nl4[e]));
             }
             const bf16x8 p0 = pack_bf16x8(s, 0), p1 = pack_bf16x8(s, 8);
 #pragma unroll

@@ -128,6 +128,48 @@ def test_block_bwd_accumulates_and_empty_cases():
     ra.ra_block_attn_bwd(e, k, k, e, e[..., 0], e[..., 0], e, dk, dv)  # no-op
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_block_bwd_rows_without_keys_mfma(D):
+    """bf16 MFMA kernels: rows whose lse is -inf contribute nothing, both where
+    they share a query tile with rows that see keys (queries start 37 positions
+    before the block's keys, lse over this block only) and where the caller
+    passes -inf for every row of a non-causal block."""
+    gh.say("ra_block_attn_bwd rows without keys", D)
+    Hq, Hkv, q_len, kv_len, off = 2, 1, 200, 150, -37
+    qn = ra_inputs.normal((1, Hq, q_len, D), 0, seed=37)
+    kn = ra_inputs.normal((1, Hkv, kv_len, D), 1, seed=37)
+    vn = ra_inputs.normal((1, Hkv, kv_len, D), 2, seed=37)
+    gn = ra_inputs.normal((1, Hq, q_len, D), 3, seed=37)
+    q, k, v, g = (gh.to_device(x, "bf16") for x in (qn, kn, vn, gn))
+    qpos = np.arange(q_len, dtype=np.int64) + off
+    want = {"dq": np.zeros((1, Hq, q_len, D)), "dk": np.zeros((1, Hkv, kv_len, D)),
+            "dv": np.zeros((1, Hkv, kv_len, D))}
+    lse = np.empty((1, Hq, q_len))
+    dlt = np.empty((1, Hq, q_len))
+    for h in range(Hq):
+        r = oracle.grads(qn[0, h], kn[0, 0], vn[0, 0], gn[0, h], q_pos=qpos, causal=True)
+        lse[0, h], dlt[0, h] = r["lse"], r["delta"]
+        want["dq"][0, h] = r["dq"]
+        want["dk"][0, 0] += r["dk"]
+        want["dv"][0, 0] += r["dv"]
+    assert np.isneginf(lse[0, :, :37]).all() and np.isfinite(lse[0, :, 37:]).all()
+    dq = torch.zeros(1, Hq, q_len, D, device="cuda")
+    dk = torch.zeros(1, Hkv, kv_len, D, device="cuda")
+    dv = torch.zeros(1, Hkv, kv_len, D, device="cuda")
+    lse_d = torch.from_numpy(lse.astype(np.float32)).cuda()
+    dlt_d = torch.from_numpy(dlt.astype(np.float32)).cuda()
+    ra.ra_block_attn_bwd(q, k, v, g, lse_d, dlt_d, dq, dk, dv, causal=True, q_pos0=off, k_pos0=0)
+    torch.cuda.synchronize()
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _close(gh.to_host_f64(got), want[name], 2e-2, name)
+    # every row -inf on a non-causal block: nothing changes
+    for x in (dq, dk, dv):
+        x.fill_(0.5)
+    ra.ra_block_attn_bwd(q, k, v, g, torch.full_like(lse_d, float("-inf")), dlt_d, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert all(bool(torch.all(x == 0.5)) for x in (dq, dk, dv))
+
+
 RING_CASES = [("striped", True, "f32", 16, 4, 64), ("contiguous", True, "f32", 16, 4, 64),
               ("contiguous", False, "f32", 32, 2, 96), ("striped", True, "bf16", 128, 4, 1024),
               ("contiguous", True, "bf16", 64, 2, 512)]
