@@ -105,19 +105,23 @@ struct TileReads {
 };
 
 // Tile copy plan: a tile of kTile rows x D bf16 is kTile*D*2/1024 copy
-// instructions of 1 KiB, PER of them for each of the WAVES waves.  Instruction
-// i of a wave covers rows crow0 + RPI i (RPI = 64 lanes / CPR chunks a row);
-// lane l fetches the global chunk that belongs at chunk position l % CPR.
+// instructions of 1 KiB (RPI = 64 lanes / CPR chunks a row), PER of them for
+// each of the WAVES waves.  Instruction i of wave w fills tile rows
+// (i WAVES + w) RPI + l / CPR (lane l), so the rows a lane fetches are 16 i'
+// apart: they share r & 15, hence the swizzle, hence the lane's byte offset
+// within a row.  A full tile then costs one per-lane offset per copy, and
+// instruction i only moves the (scalar) base pointer.
 template <int D, int WAVES>
 struct TileCopy {
     static constexpr int CPR = D / 8;
     static constexpr int RPI = 64 / CPR;
     static constexpr int BYTES = kTile * D * 2;
     static constexpr int PER = BYTES / 1024 / WAVES;
-    int crow0, cpos;
+    static_assert((WAVES * RPI) % 16 == 0, "rows a lane fetches must share the swizzle period");
+    int crow0, cpos;  // this lane's first row and its chunk position
     __device__ void init(int wave, int lane) {
-        crow0 = wave * PER * RPI + lane / CPR;
-        cpos = lane % CPR;
+        crow0 = wave * RPI + lane / CPR;
+        cpos = (lane % CPR) ^ swz<D>(crow0);
     }
     // The same plan with the lane index recomputed at the call (volatile, so
     // the compiler cannot hoist it and keep crow0 / cpos live through a loop
@@ -134,12 +138,18 @@ struct TileCopy {
     __device__ void issue(const uint16_t* src, int64_t stride, int r0, int n_rows, uint32_t lds, int wave) const {
         const uint16_t* base = src + static_cast<int64_t>(r0) * stride;
         const int last = n_rows - 1 - r0;
+        const uint32_t s2 = static_cast<uint32_t>(stride * 2);
+        if (last >= kTile - 1) {  // whole tile inside the block
+            const uint32_t o = crow0 * s2 + cpos * 16;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int crow = crow0 + RPI * i;
-            const int cchunk = cpos ^ swz<D>(crow);
-            const uint32_t o = static_cast<uint32_t>(min(crow, last) * stride * 2 + cchunk * 16);
-            lds_dma16(base, o, lds + (wave * PER + i) * 1024);
+            for (int i = 0; i < PER; ++i)
+                lds_dma16(base + static_cast<int64_t>(i) * WAVES * RPI * stride, o, lds + (i * WAVES + wave) * 1024);
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const uint32_t o = static_cast<uint32_t>(min(crow0 + i * WAVES * RPI, last)) * s2 + cpos * 16;
+                lds_dma16(base, o, lds + (i * WAVES + wave) * 1024);
+            }
         }
     }
 };
