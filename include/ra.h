@@ -217,7 +217,9 @@ ra_status ra_ring_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * its partial straight into the running state; every later step merges its
  * block into that state (in the block kernel, or -- with separate_merge -- by
  * a partial plus an ra_lse_merge fold); a final ra_lse_merge pass normalises
- * (fused schedule) or the last fold does (separate schedule).  Fully masked
+ * (fused schedule) or the last fold does (separate schedule).  With key splits
+ * (kv_splits) every step writes one partial per key range and one merge pass
+ * folds them all into the running state, the last one also normalising.  Fully masked
  * (position, block) pairs are skipped (contiguous causal: blocks after the
  * query block).  Positions are spread over n_streams library-owned streams.
  *
