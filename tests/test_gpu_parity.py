@@ -392,6 +392,12 @@ def test_kv_split_ring_matches_oracle(lay, causal, D, Sb, N, splits, used):
     assert torch.max(torch.abs(l1 - l2)) <= 1e-4
     hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
     gh.compare_rows(o1, l1, qn, kn, vn, hh.ravel(), tt.ravel(), N, lay, 0, causal, "bf16")
+    # the same key ranges with blocks travelling through the emulated-transfer
+    # slots on one stream: the same schedule, so bit-identical
+    o3, l3, st3 = gh.run_ring(qs, ks, vs, N, 0, lay, causal, kv_splits=splits, emulate_copy=True, n_streams=1,
+                              stats=True)
+    assert st3["kv_splits"] == used
+    assert torch.equal(o3, o1) and torch.equal(l3, l1)
 
 
 @pytest.mark.parametrize("splits", [0, 1])
