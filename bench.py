@@ -79,10 +79,12 @@ def _openmp():
         return None
 
 
-def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2, threads=None):
+def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2, threads=None, g_rows_fn=None):
     """Time the oracle on seeded query rows of the workload, in chunks of 32 rows,
     until about budget_s seconds of CPU work have been done.  threads=None uses
-    every host core the process may run on."""
+    every host core the process may run on.  With g_rows_fn (the rows' output
+    gradients) the oracle computes the rows' dQ instead of their output: it
+    forms the scores, lse, D = dO . O and dQ, 8 d FLOPs a visible pair."""
     import oracle
 
     gomp = _openmp()
@@ -106,18 +108,25 @@ def cpu_baseline(cfg, k_np, v_np, q_rows_fn, budget_s, max_rows=20000, seed=2, t
             t = rng.integers(0, S, 32)
         t = np.sort(t).astype(np.int64)
         qr = q_rows_fn(h, t)
+        gr = g_rows_fn(h, t) if g_rows_fn is not None else None
         t0 = time.perf_counter()
-        oracle.rows(qr, k_np[0, h // g], v_np[0, h // g], q_pos=t, causal=cfg["causal"])
+        if gr is None:
+            oracle.rows(qr, k_np[0, h // g], v_np[0, h // g], q_pos=t, causal=cfg["causal"])
+        else:
+            oracle.grads(qr, k_np[0, h // g], v_np[0, h // g], gr, q_pos=t, causal=cfg["causal"], key_grads=False)
         dt += time.perf_counter() - t0
         pairs += int(np.sum(t + 1)) if cfg["causal"] else len(t) * S
         rows += len(t)
-    flops = 4.0 * cfg["D"] * pairs
+    per_pair = 4.0 if g_rows_fn is None else 8.0
+    flops = per_pair * cfg["D"] * pairs
+    what = "output" if g_rows_fn is None else "dQ (scores, lse, D = dO . O and dQ: 8 d FLOPs a pair)"
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} seeded query rows of this workload (one head per 32-row chunk), each over its "
-                      f"full causal key range, fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
+            "sample": f"{rows} seeded query rows of this workload (one head per 32-row chunk), their {what} over "
+                      f"the full causal key range, fp64: {flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
-def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev):
+def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev, k_np, v_np,
+                 q_rows):
     """Time ra_ring_backward over the workload: one forward provides o and lse,
     then each timed step is the whole backward (delta, every block pair's
     dQ / dK / dV share).  FLOPs: 10 head_dim per unmasked pair (five products)."""
@@ -187,6 +196,19 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                                "timed ones"},
         "cpu_baseline": None,
     }
+    if args.cpu_seconds > 0:
+        if g_np is not None:
+            def g_rows(h, t):
+                r = (t - first) // N if lay == "striped" else t - first * sb
+                return g_np[0][0][h, r]
+        else:
+            def g_rows(h, t):
+                return g_full[0][h, t]
+        log(f"cpu baseline: oracle dQ rows for about {args.cpu_seconds:.0f} s on all cores")
+        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds, g_rows_fn=g_rows)
+        # the oracle over one whole backward step at the measured rate (extrapolated; 10 d a pair)
+        cpu["extrapolated_step_s"] = round(flops_per_step / (cpu["value"] * 1e12), 1)
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
@@ -318,7 +340,7 @@ def main():
         return st
 
     if args.backward:
-        run_backward(args, cfg, ra, torch, step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev)
+        run_backward(args, cfg, ra, torch, step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev, k_np, v_np, q_rows)
         return
 
     log(f"warmup {args.warmup}")
