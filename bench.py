@@ -54,10 +54,11 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per block-kernel launch from committed rocprofv3 counters, if they
-    were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "block_attn_traffic.json")
+def traffic_from_profile(kernel_src, record="block_attn_traffic.json"):
+    """HBM bytes per block-kernel launch (or block pair, for the backward) from
+    committed rocprofv3 counters, if they were taken on the current kernel
+    source (else None)."""
+    path = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -189,7 +190,10 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                    "causal": cfg["causal"], "positions_run": n_run, "first_position": first,
                    "unmasked_flops_per_step": flops_per_step},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc",
+                                                                  "block_attn_bwd_mfma.hip"),
+                                                     "block_attn_bwd_traffic.json"),
                      "kernel": "dq_kernel + dkdv_kernel (one block pair)", "launches": tot["block_launches"],
                      "mean_launch_ms": round(per_launch_ms, 4),
                      "timing": "HIP events around each block pair's pair of launches, 3 steps after the "

@@ -67,6 +67,19 @@ __device__ inline bf16x8 ld_tr(const lds_char* lo, const lds_char* hi) {
 
 #define MFMA(a, b, c) __builtin_amdgcn_mfma_f32_32x32x16_bf16((a), (b), (c), 0, 0, 0)
 
+#ifndef RA_BWD_XCD_REMAP
+#define RA_BWD_XCD_REMAP 1
+#endif
+// Workgroup id -> logical tile id so that consecutive logical ids (one head's
+// tiles, which stream the same operand rows) share an XCD and its L2: the
+// dispatcher deals workgroups round-robin over the 8 XCDs.  A bijection on
+// [0, n).
+__device__ inline int64_t xcd_tile(int64_t w, int64_t n) {
+    if (!RA_BWD_XCD_REMAP) return w;
+    const int64_t q = n / 8, r = n % 8, x = w % 8, i = w / 8;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
 // Per-lane LDS byte offsets of both read kinds for a tile of D-element rows.
 // Row reads: lane l reads row 32 sub + (l%32), chunk 2 kb + l/32, stored at
 // chunk position (2 kb + h) ^ swz(l%32) = 2 (kb ^ (swz >> 1)) + (h ^ (swz & 1)),
@@ -166,11 +179,13 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
     const int tid = threadIdx.x, lane = tid & 63, qi = lane & 31, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_qt = (a.q_len + kMq - 1) / kMq;
-    int64_t L = blockIdx.x;
-    const int qt_rank = static_cast<int>(L % n_qt);
+    // (64-bit divisions expand to vector code: the results are made scalar
+    // again, as the copy addresses need wave-uniform bases)
+    int64_t L = xcd_tile(blockIdx.x, static_cast<int64_t>(n_qt) * a.Hq * a.B);
+    const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % n_qt));
     L /= n_qt;
-    const int h = static_cast<int>(L % a.Hq);
-    const int b = static_cast<int>(L / a.Hq);
+    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.Hq));
+    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / a.Hq));
     const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
     const int hk = h / (a.Hq / a.Hkv);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
@@ -307,11 +322,11 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_kt = (a.kv_len + kMk - 1) / kMk;
-    int64_t L = blockIdx.x;
-    const int kt_rank = static_cast<int>(L % n_kt);
+    int64_t L = xcd_tile(blockIdx.x, static_cast<int64_t>(n_kt) * a.Hkv * a.B);
+    const int kt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % n_kt));
     L /= n_kt;
-    const int hk = static_cast<int>(L % a.Hkv);
-    const int b = static_cast<int>(L / a.Hkv);
+    const int hk = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.Hkv));
+    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / a.Hkv));
     const int kt = kt_rank;  // causal: earlier keys see more rows, so these come first
     const int grp = a.Hq / a.Hkv;
     const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1];
