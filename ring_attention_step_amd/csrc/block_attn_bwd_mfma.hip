@@ -30,9 +30,10 @@
 // registers.  Tiles are row-major in LDS with 16-byte chunk c of row r at
 // chunk position c ^ swz(r) (conflict-free for both read kinds on gfx950's 64
 // banks), copied HBM -> LDS by global_load_lds_dwordx4 into double buffers.
-// Two workgroups of four waves share a CU, so one workgroup's MFMAs overlap
-// the other's vector work (eight-wave workgroups sharing each tile measured
-// slower).
+// dq_kernel runs eight waves in the forward kernel's ping-pong (two groups
+// of one wave per SIMD, half a tile apart); for dkdv_kernel two workgroups
+// of four waves share a CU, so one workgroup's MFMAs overlap the other's
+// vector work.
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -47,7 +48,7 @@ using namespace mfma;
 
 // Waves per workgroup of each kernel (compile-time knobs; defaults measured best).
 #ifndef RA_BWD_DQ_WAVES
-#define RA_BWD_DQ_WAVES 4
+#define RA_BWD_DQ_WAVES 8
 #endif
 #ifndef RA_BWD_KV_WAVES
 #define RA_BWD_KV_WAVES 4
@@ -168,19 +169,35 @@ struct TileCopy {
 };
 
 // --------------------------------------------------------------------- dQ
+// Eight waves in two groups of one wave per SIMD, half a tile apart
+// ("ping-pong", as in the forward kernel): between consecutive barriers one
+// group runs its MFMA stream -- dQ^T += K^T dS^T of tile t-1, then S^T and
+// dP^T of tile t -- while the other computes dS of its current tile on the
+// vector ALU.  K tile t is read in phases 2t..2t+3 (S^T, then dQ^T one tile
+// later), V tile t in phases 2t..2t+1; K and V have three LDS buffers each.
+// Group 0's stream (phase 2t) copies K(t+1) into K buffer (t+1) mod 3, whose
+// last reader finished in phase 2t-1; it is awaited by the barrier ending
+// phase 2t+1 and first read in phase 2t+2.  Group 1's stream (phase 2t+1)
+// copies V(t+2) into V buffer (t+2) mod 3 (last read in phase 2t-1); group 1
+// lets a phase's own copies stay in flight and awaits them by the barrier
+// ending phase 2t+3, before their first reader in phase 2t+4.  Either way a
+// copy has two phases to land.
 template <int D>
-__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
-    const BwdArgs a) {
-    constexpr int kMq = 32 * kDqWaves;  // query rows per workgroup
+__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(const BwdArgs a) {
+    constexpr int WAVES = kDqWaves;
+    static_assert(WAVES == 8, "ping-pong needs two groups of one wave per SIMD");
+    constexpr int kMq = 32 * WAVES;  // query rows per workgroup
     constexpr int SUB = kTile / 32;
-    constexpr int TB = TileCopy<D, kDqWaves>::BYTES;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // {K, V} x 2 buffers
+    constexpr int CPR = D / 8;
+    constexpr int TB = kTile * D * 2;                 // one K or V tile
+    constexpr int PER_G = TB / 1024 / (WAVES / 2);    // copy instructions per wave of a group
+    constexpr int RPI = 64 / CPR;
+    __shared__ __attribute__((aligned(1024))) char smem[6 * TB];  // K0 K1 K2 V0 V1 V2
 
     const int tid = threadIdx.x, lane = tid & 63, qi = lane & 31, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int group = wave / (WAVES / 2), wslot = wave % (WAVES / 2);
     const int n_qt = (a.q_len + kMq - 1) / kMq;
-    // (64-bit divisions expand to vector code: the results are made scalar
-    // again, as the copy addresses need wave-uniform bases)
     int64_t L = xcd_tile(blockIdx.x, static_cast<int64_t>(n_qt) * a.Hq * a.B);
     const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % n_qt));
     L /= n_qt;
@@ -206,9 +223,6 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
         greg[kb] = row_ok ? *reinterpret_cast<const bf16x8*>(gp + row * a.dos[2] + kb * 16 + half * 8) : bf16x8{};
     }
     const float lse2 = row_ok ? a.lse[row0 + row] * kLog2e : -INFINITY;
-    // exp2 argument offset: -lse (log2 units), or -inf for a row that sees no
-    // key at all (and for rows past the block), which makes every p exactly 0
-    const float nl2 = lse2 == -INFINITY ? -INFINITY : -lse2;
     const float dlt = row_ok ? a.delta[row0 + row] : 0.f;
     const float c2 = a.scale * kLog2e;
 
@@ -226,72 +240,149 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
 
     TileReads<D> rd;
     rd.init(lane);
-    TileCopy<D, kDqWaves> cp;
-    cp.init(wave, lane);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     const lds_char* lds = RA_LDS_PTR(char, smem);
+    // copy plan of one group: instruction i of wave slot w covers rows crow0 + RPI i
+    const int crow0 = wslot * PER_G * RPI + lane / CPR;
+    const int cpos = lane % CPR;
 
     f32x16 acc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+    f32x16 s[SUB], dp[SUB];
+    bf16x8 dsr[2 * SUB];
+#pragma unroll
+    for (int i = 0; i < 2 * SUB; ++i) dsr[i] = bf16x8{};
 
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const uint32_t buf = lds0 + (t & 1) * 2 * TB;
-        cp.issue(kp, a.ks[2], t * kTile, a.kv_len, buf, wave);
-        cp.issue(vp, a.vs[2], t * kTile, a.kv_len, buf + TB, wave);
+    // MFMA stream of one phase: dQ of tile tp (K buffer kbp), then S^T and dP^T
+    // of tile tq (K buffer kbq, V buffer vbq), software-pipelined: each LDS
+    // operand is read kPf steps ahead of its MFMA.
+    constexpr int kPf = 4;
+    constexpr int NDQ = (kTile / 16) * (D / 32), NSP = 2 * SUB * (D / 16), NT = NDQ + NSP;
+    auto mfma_stream = [&](int kbp, int kbq, int vbq, auto&& hook) __attribute__((always_inline)) {
+        const lds_char* kp_t = lds + kbp * TB;
+        const lds_char* kq_t = lds + kbq * TB;
+        const lds_char* vq_t = lds + (3 + vbq) * TB;  // vbq: V buffer 0..2
+        auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+            if (i < NDQ) return rd.cols(kp_t, i / (D / 32), i % (D / 32));
+            const int j = i - NDQ, kb = j / (2 * SUB), r = j % (2 * SUB);
+            return rd.rows(r < SUB ? kq_t : vq_t, r % SUB, kb);
+        };
+        auto run = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+            if (i < NDQ) {
+                const int kb2 = i / (D / 32), dblk = i % (D / 32);
+                acc[dblk] = MFMA(op, dsr[kb2], acc[dblk]);
+            } else {
+                const int j = i - NDQ, kb = j / (2 * SUB), r = j % (2 * SUB), sub = r % SUB;
+                if (r < SUB) s[sub] = MFMA(op, qreg[kb], kb == 0 ? f32x16{} : s[sub]);
+                else dp[sub] = MFMA(op, greg[kb], kb == 0 ? f32x16{} : dp[sub]);
+            }
+        };
+        bf16x8 ops[kPf];
+#pragma unroll
+        for (int n = 0; n < kPf; ++n) ops[n] = load_op(n);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const bf16x8 op = ops[n % kPf];
+            if (n + kPf < NT) ops[n % kPf] = load_op(n + kPf);
+            run(n, op);
+            hook(n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
-    if (n_tiles > 0) issue(0);
-    for (int t = 0; t < n_tiles; ++t) {
-        wait_vmem_all();
-        __syncthreads();
-        if (t + 1 < n_tiles) issue(t + 1);
+
+    // dS of tile t from this wave's S^T, dP^T (zero where nothing is visible).
+    // Masked scores become -inf before one branch-free exp2 loop.
+    const float nl2 = lse2 == -INFINITY ? -INFINITY : -lse2;
+    auto valu_half = [&](int t) __attribute__((always_inline)) {
         const int kbase = t * kTile;
-        if (kbase >= wave_key_end) continue;  // nothing this wave sees (wave-uniform)
-        const lds_char* kt = lds + (t & 1) * 2 * TB;
-        const lds_char* vt = kt + TB;
-        f32x16 s[SUB], dp[SUB];
+        if (t < n_tiles && kbase < wave_key_end) {
+            if (kbase + kTile > wave_full_end) {  // diagonal or ragged tile
+                const int k_lim = a.kv_len - kbase - 4 * half;
+                const int c_lim = a.causal ? row + a.mask_offset - kbase - 4 * half : k_lim;
 #pragma unroll
-        for (int sub = 0; sub < SUB; ++sub) {
-            s[sub] = f32x16{};
-            dp[sub] = f32x16{};
+                for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) {
-                s[sub] = MFMA(rd.rows(kt, sub, kb), qreg[kb], s[sub]);
-                dp[sub] = MFMA(rd.rows(vt, sub, kb), greg[kb], dp[sub]);
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = sub * 32 + 8 * (v / 4) + (v % 4);
+                        s[sub][v] = ((j < k_lim) & (j <= c_lim)) ? s[sub][v] : -INFINITY;
+                    }
+            }
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    s[sub][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], c2, nl2)) * (dp[sub][v] - dlt);
+                dsr[2 * sub] = pack_bf16x8(s[sub], 0);
+                dsr[2 * sub + 1] = pack_bf16x8(s[sub], 8);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * SUB; ++i) dsr[i] = bf16x8{};
+        }
+    };
+
+    constexpr int kStep = (NT / 2) / PER_G;
+    static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
+    if (n_tiles > 0) {
+        // finite K buffer for the dQ product of "tile -1" (dS = 0 there)
+        for (int i = tid; i < TB / 16; i += 64 * WAVES)
+            *(__attribute__((address_space(3))) s16x8*)(lds + 2 * TB + i * 16) = s16x8{};
+        // K(0), V(0), V(1), copied by all eight waves (indices clamped to the block)
+        {
+            const int per = TB / 1024 / WAVES;
+            for (int i = 0; i < per; ++i) {
+                const int pos = (wave * per + i) * 64 + lane;
+                const int cr = pos / CPR, cc = (pos % CPR) ^ swz<D>(cr);
+                const uint32_t dst = (wave * per + i) * 1024;
+                lds_dma16(kp, static_cast<uint32_t>(min(cr, a.kv_len - 1) * a.ks[2] * 2 + cc * 16), lds0 + dst);
+                lds_dma16(vp, static_cast<uint32_t>(min(cr, a.kv_len - 1) * a.vs[2] * 2 + cc * 16),
+                          lds0 + 3 * TB + dst);
+                const int t1 = min(1, n_tiles - 1);
+                lds_dma16(vp + static_cast<int64_t>(t1) * kTile * a.vs[2],
+                          static_cast<uint32_t>(min(cr, a.kv_len - 1 - t1 * kTile) * a.vs[2] * 2 + cc * 16),
+                          lds0 + 4 * TB + dst);
             }
         }
-        // Mask (diagonal / ragged tiles only): masked scores become -inf, so
-        // that their exp2 below is exactly 0 (the scale is positive).
-        // Register v of sub-tile sub holds key kbase + 4 half + j, with the
-        // compile-time j = 32 sub + 8 (v/4) + v%4: visible iff
-        // j < kv_len - kbase - 4 half and (causal) j <= row + mask_offset - kbase - 4 half.
-        if (kbase + kTile > wave_full_end) {
-            const int k_lim = a.kv_len - kbase - 4 * half;
-            const int c_lim = a.causal ? row + a.mask_offset - kbase - 4 * half : k_lim;
-#pragma unroll
-            for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int j = sub * 32 + 8 * (v / 4) + (v % 4);
-                    s[sub][v] = ((j < k_lim) & (j <= c_lim)) ? s[sub][v] : -INFINITY;
+        wait_vmem_all();
+        __syncthreads();
+        if (group == 1) __syncthreads();
+        int kb_prev = 2, kb_cur = 0;  // K buffers of tiles t-1 and t (t mod 3)
+        int vb_cur = 0, vb_next2 = 2;  // V buffers of tiles t and t+2
+        for (int t = 0; t <= n_tiles; ++t) {
+            const int kb_next = kb_cur == 2 ? 0 : kb_cur + 1;
+            // this group's copy: K(t+1) (group 0) or V(t+2) (group 1); index clamped
+            const bool gk = group == 0;
+            const int tc = min(t + (gk ? 1 : 2), n_tiles - 1);
+            const int64_t stride = gk ? a.ks[2] : a.vs[2];
+            const uint16_t* src = (gk ? kp : vp) + static_cast<int64_t>(tc) * kTile * stride;
+            const uint32_t stride2 = static_cast<uint32_t>(stride * 2);
+            const int last = a.kv_len - 1 - tc * kTile;
+            const uint32_t dst = lds0 + (gk ? kb_next : 3 + vb_next2) * TB + wslot * PER_G * 1024;
+            __builtin_amdgcn_s_setprio(1);
+            mfma_stream(kb_prev, kb_cur, vb_cur, [&](int n) __attribute__((always_inline)) {
+                if (n % kStep == 0 && n / kStep < PER_G) {
+                    const int i = n / kStep;
+                    const int crow = crow0 + RPI * i;
+                    const uint32_t o = static_cast<uint32_t>(min(crow, last)) * stride2 +
+                                       static_cast<uint32_t>((cpos ^ swz<D>(crow)) * 16);
+                    lds_dma16(src, o, dst + i * 1024);
                 }
+            });
+            __builtin_amdgcn_s_setprio(0);
+            if (group == 1) wait_vmem_leave<PER_G>();  // the previous phase's V copies have landed
+            __syncthreads();
+            valu_half(t);
+            if (group == 0) wait_vmem_all();
+            __syncthreads();
+            kb_prev = kb_cur;
+            kb_cur = kb_next;
+            vb_cur = vb_cur == 2 ? 0 : vb_cur + 1;
+            vb_next2 = vb_next2 == 2 ? 0 : vb_next2 + 1;
         }
-        // dS^T = P^T (dP^T - delta)
-        bf16x8 dsr[2 * SUB];
-#pragma unroll
-        for (int sub = 0; sub < SUB; ++sub) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                s[sub][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sub][v], c2, nl2)) * (dp[sub][v] - dlt);
-            dsr[2 * sub] = pack_bf16x8(s[sub], 0);
-            dsr[2 * sub + 1] = pack_bf16x8(s[sub], 8);
-        }
-#pragma unroll
-        for (int kb2 = 0; kb2 < kTile / 16; ++kb2)
-#pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk) acc[dblk] = MFMA(rd.cols(kt, kb2, dblk), dsr[kb2], acc[dblk]);
+        if (group == 0) __syncthreads();
+        wait_vmem_all();  // group 1's last copies land before the workgroup's LDS is released
     }
-    wait_vmem_all();
 
     if (row_ok) {
         float* out = a.dq + (row0 + row) * D;
@@ -299,12 +390,12 @@ __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2
         for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                f32x4* dst = reinterpret_cast<f32x4*>(out + dblk * 32 + 8 * g + 4 * half);
-                const f32x4 prev = *dst;
-                *dst = f32x4{__builtin_fmaf(a.scale, acc[dblk][4 * g], prev[0]),
-                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 1], prev[1]),
-                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 2], prev[2]),
-                             __builtin_fmaf(a.scale, acc[dblk][4 * g + 3], prev[3])};
+                f32x4* dstp = reinterpret_cast<f32x4*>(out + dblk * 32 + 8 * g + 4 * half);
+                const f32x4 prev = *dstp;
+                *dstp = f32x4{__builtin_fmaf(a.scale, acc[dblk][4 * g], prev[0]),
+                              __builtin_fmaf(a.scale, acc[dblk][4 * g + 1], prev[1]),
+                              __builtin_fmaf(a.scale, acc[dblk][4 * g + 2], prev[2]),
+                              __builtin_fmaf(a.scale, acc[dblk][4 * g + 3], prev[3])};
             }
     }
 }
