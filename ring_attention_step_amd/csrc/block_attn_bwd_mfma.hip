@@ -31,9 +31,9 @@
 // chunk position c ^ swz(r) (conflict-free for both read kinds on gfx950's 64
 // banks), copied HBM -> LDS by global_load_lds_dwordx4 into double buffers.
 // dq_kernel runs eight waves in the forward kernel's ping-pong (two groups
-// of one wave per SIMD, half a tile apart); for dkdv_kernel two workgroups
-// of four waves share a CU, so one workgroup's MFMAs overlap the other's
-// vector work.
+// of one wave per SIMD, half a tile apart); dkdv_kernel runs eight waves
+// (256 keys) that share each query tile, two per SIMD, whose MFMAs and
+// vector work interleave as they fall.
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -51,7 +51,7 @@ using namespace mfma;
 #define RA_BWD_DQ_WAVES 8
 #endif
 #ifndef RA_BWD_KV_WAVES
-#define RA_BWD_KV_WAVES 4
+#define RA_BWD_KV_WAVES 8
 #endif
 constexpr int kDqWaves = RA_BWD_DQ_WAVES;
 constexpr int kKvWaves = RA_BWD_KV_WAVES;
