@@ -54,10 +54,10 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def traffic_from_profile(kernel_src, record="block_attn_traffic.json"):
+def traffic_from_profile(kernel_src, workload, record="block_attn_traffic.json"):
     """HBM bytes per block-kernel launch (or block pair, for the backward) from
     committed rocprofv3 counters, if they were taken on the current kernel
-    source (else None)."""
+    source and on this workload (else None)."""
     path = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(path):
         return None
@@ -65,7 +65,7 @@ def traffic_from_profile(kernel_src, record="block_attn_traffic.json"):
         rec = json.load(f)
     with open(kernel_src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_sha256") != digest:
+    if rec.get("kernel_sha256") != digest or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -193,7 +193,7 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc",
                                                                   "block_attn_bwd_mfma.hip"),
-                                                     "block_attn_bwd_traffic.json"),
+                                                     args.workload, "block_attn_bwd_traffic.json"),
                      "kernel": "dq_kernel + dkdv_kernel (one block pair)", "launches": tot["block_launches"],
                      "mean_launch_ms": round(per_launch_ms, 4),
                      "timing": "HIP events around each block pair's pair of launches, 3 steps after the "
@@ -411,7 +411,8 @@ def main():
     per_launch_flops = rt["flops"] / max(1, rt["block_launches"])
     per_launch_ms = rt["block_ms"] / max(1, rt["block_launches"])
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
-    traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"))
+    traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"),
+                                   args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",

@@ -395,11 +395,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // reader's phase.
     static_assert(WAVES % 8 == 0, "ping-pong needs two groups of one wave per SIMD");
     const int group = wave / (WAVES / 2);
-    // The MFMA half always runs the full stream: for a tile this wave cannot
-    // see, P is zero (valu_half) and the V buffers hold finite values (zeroed
-    // below before any copy), so the PV product adds exactly zero, and scores
-    // of an unseen tile are never read.  A group's phase lasts as long as its
-    // slowest wave, so skipping would not shorten it.
+    // The MFMA half runs the full stream even for a tile this wave cannot see:
+    // P is then zero (valu_half) and the V tile holds finite block values, so
+    // the PV product adds exactly zero, and scores of an unseen tile are never
+    // read.  A group's phase lasts as long as its slowest wave, so skipping
+    // would not shorten it.  Only the first MFMA half (no PV product yet) and
+    // the one after the last tile (no QK^T, no copies) are shortened.
     // Copies.  Group 0's MFMA half of tile t (global phase 2t) copies K(t+1);
     // group 1's (phase 2t+1) copies V(t).  Both buffers' last readers
     // finished in phase 2t-1, both tiles are awaited at the end of phase
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // others), and rows past the block re-read its last row.
     constexpr int kStep = (NT / 2) / PER_G;
     static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
-    auto mfma_half = [&](int t) __attribute__((always_inline)) {
+    auto mfma_half = [&]<bool PV, bool QK>(int t) __attribute__((always_inline)) {
         const bool gk = group == 0;
         const int tt = gk ? t + 1 : t;
         const int tc = min(tt, n_tiles - 1);
@@ -422,8 +423,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         const int last = kv_len - 1 - tc * kNk;  // last row of the block within tile tc
         const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
         if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        mfma_stream.template operator()<true, true>(t - 1, t, [&](int n) __attribute__((always_inline)) {
-            if (n % kStep == 0 && n / kStep < PER_G) {
+        mfma_stream.template operator()<PV, QK>(t - 1, t, [&](int n) __attribute__((always_inline)) {
+            if (QK && n % kStep == 0 && n / kStep < PER_G) {
                 const int i = n / kStep;
                 const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
                 lds_dma16(src, o, dst + i * 1024);
@@ -441,29 +442,36 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     };
     // Both groups run the same loop body -- MFMA half of tile t, barrier,
     // softmax half of tile t, barrier -- but group 1 first passes one extra
-    // barrier (and group 0 one at the end), so group 1 runs one phase behind.
+    // barrier (and group 0 one after its final PV half), so group 1 runs one
+    // phase behind and both groups pass the same number of barriers.
     // Global phase 2t carries group 0's MFMA half of tile t and group 1's
     // softmax half of tile t-1; phase 2t+1 the other way round.  The copies of
     // K(t+1) and V(t) start in phase 2t (each group issues its share from the
     // half that falls there) and are awaited at the end of phase 2t+1.
     if (n_tiles > 0) {
-        // finite V buffers and P^T = 0 before the first PV product
-        for (int i = tid; i < 2 * TILE_BYTES / 16; i += 64 * WAVES)
-            *(__attribute__((address_space(3))) s16x8*)(lds + 2 * TILE_BYTES + i * 16) = s16x8{};
-#pragma unroll
-        for (int i = 0; i < 2 * kSub; ++i) preg[i] = bf16x8{};
         issue_k(0);
         wait_vmem_all();
         __syncthreads();
         if (group == 1) __syncthreads();
-        for (int t = 0; t <= n_tiles; ++t) {
-            mfma_half(t);
+        // first tile: no PV product yet
+        mfma_half.template operator()<false, true>(0);
+        if (group == 1) wait_vmem_all();
+        __syncthreads();
+        valu_half(0);
+        if (group == 0) wait_vmem_all();
+        __syncthreads();
+        for (int t = 1; t < n_tiles; ++t) {
+            mfma_half.template operator()<true, true>(t);
             if (group == 1) wait_vmem_all();
             __syncthreads();
             valu_half(t);
             if (group == 0) wait_vmem_all();
             __syncthreads();
         }
+        // PV product of the last tile (no copies).  Group 0 then passes the
+        // barrier that ends group 1's last softmax half; group 1 runs its
+        // final PV half with no barrier after it, while group 0 writes out.
+        mfma_half.template operator()<true, false>(n_tiles);
         if (group == 0) __syncthreads();
     }
 #else
