@@ -47,9 +47,9 @@
 // Work decomposition: a workgroup of WAVES (8) waves owns 32*WAVES query rows
 // of one (b, q-head); each wave owns 32 rows.  Keys are visited in tiles of
 // kNk.  Waves w and w + 4 share a SIMD; they form two groups run half a tile
-// apart ("ping-pong"), so while one wave of a SIMD issues MFMAs (the PV
-// product of the previous tile, then QK^T of the current one) the other runs
-// its softmax on the vector ALU.  Each MFMA half is one software-pipelined
+// apart ("ping-pong"), so while one wave of a SIMD issues MFMAs (QK^T of the
+// current tile, then the PV product of the previous one) the other runs its
+// softmax on the vector ALU.  Each MFMA half is one software-pipelined
 // stream in which every operand's LDS read is issued a few MFMAs ahead of its
 // use.  Causal masking uses the block's mask offset: tiles past the
 // workgroup's last visible key are never loaded, and the element mask is
@@ -80,7 +80,7 @@ using namespace mfma;
 #define RA_MFMA_PINGPONG 1
 #endif
 #ifndef RA_MFMA_PREFETCH
-#define RA_MFMA_PREFETCH 4
+#define RA_MFMA_PREFETCH 3
 #endif
 constexpr int kNk = RA_MFMA_NK;  // keys per tile (64 or 128)
 constexpr int kSub = kNk / 32;   // 32-key sub-tiles per tile
@@ -336,31 +336,39 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         }
     };
 
-    // One MFMA half as a software-pipelined operand stream: the PV MFMAs of
-    // tile tp (O^T += V^T P^T, 4-k-block x dblk order) then the QK^T MFMAs of
-    // tile tq (kb-major, sub-tile-minor).  Each operand's LDS read is issued
-    // kPf steps before its MFMA, and a scheduling fence after every step keeps
-    // that distance, so LDS latency hides behind the MFMAs in flight.
+    // One MFMA half as a software-pipelined operand stream: the QK^T MFMAs of
+    // tile tq (kb-major, sub-tile-minor) then the PV MFMAs of tile tp
+    // (O^T += V^T P^T, 4-k-block x dblk order).  Each operand's LDS read is
+    // issued kPf steps before its MFMA, and a scheduling fence after every step
+    // keeps that distance, so LDS latency hides behind the MFMAs in flight.
     constexpr int kPf = RA_MFMA_PREFETCH;
     constexpr int NPV = 2 * kSub * (D / 32), NQK = kSub * (D / 16), NT = NPV + NQK;
-    auto mfma_stream = [&]<bool PV, bool QK>(int tp, int tq, auto&& hook) __attribute__((always_inline)) {
+    bf16x8 ops[kPf];  // operands in flight (the first ones may be issued before a barrier)
+    auto load_op_at = [&](const lds_char* vst, const lds_char* kst, int i) __attribute__((always_inline)) -> bf16x8 {
+        if (i < NPV) {
+            const int kb2 = i / (D / 32), dblk = i % (D / 32);
+            const int run = (kb2 * 16) * CPR * 16;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vst + voff_lo[dblk] + run));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vst + voff_hi[dblk] + run));
+            const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, both);
+        }
+        const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
+        return *(const __attribute__((address_space(3))) bf16x8*)(kst + koff[kb] + sub * 32 * CPR * 16);
+    };
+    // the first kPf operands of a full stream for tile tq (QK^T reads of K(tq))
+    auto preload = [&](int tq) __attribute__((always_inline)) {
+        const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
+#pragma unroll
+        for (int n = 0; n < kPf; ++n) ops[n] = load_op_at(nullptr, kst, NPV + n);
+    };
+    auto mfma_stream = [&]<bool PV, bool QK, bool PRE = false>(int tp, int tq, auto&& hook) __attribute__((always_inline)) {
         constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NT : NPV, N = I1 - I0;
         const lds_char* vst = lds + (2 + (tp & 1)) * TILE_BYTES;
         const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
-        auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-            if (i < NPV) {
-                const int kb2 = i / (D / 32), dblk = i % (D / 32);
-                const int run = (kb2 * 16) * CPR * 16;
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vst + voff_lo[dblk] + run));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4*)(vst + voff_hi[dblk] + run));
-                const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                return __builtin_bit_cast(bf16x8, both);
-            }
-            const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
-            return *(const __attribute__((address_space(3))) bf16x8*)(kst + koff[kb] + sub * 32 * CPR * 16);
-        };
+        auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 { return load_op_at(vst, kst, i); };
         auto run_mfma = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
             if (i < NPV) {
                 const int kb2 = i / (D / 32), dblk = i % (D / 32);
@@ -371,14 +379,22 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
                                                                      0, 0);
             }
         };
-        bf16x8 ops[kPf];
+        // step n -> operand index: QK^T first, then PV, so that the scores the
+        // wave's next softmax half reads are complete when the stream ends
+        // (only PV results, not needed until the next MFMA half, drain then)
+        auto idx = [&](int n) __attribute__((always_inline)) {
+            if constexpr (PV && QK) return n < NQK ? NPV + n : n - NQK;
+            else return I0 + n;
+        };
+        if constexpr (!PRE) {
 #pragma unroll
-        for (int n = 0; n < kPf && n < N; ++n) ops[n] = load_op(I0 + n);
+            for (int n = 0; n < kPf && n < N; ++n) ops[n] = load_op(idx(n));
+        }
 #pragma unroll
         for (int n = 0; n < N; ++n) {
             const bf16x8 op = ops[n % kPf];
-            if (n + kPf < N) ops[n % kPf] = load_op(I0 + n + kPf);
-            run_mfma(I0 + n, op);
+            if (n + kPf < N) ops[n % kPf] = load_op(idx(n + kPf));
+            run_mfma(idx(n), op);
             hook(n);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -387,8 +403,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 
 #if RA_MFMA_PINGPONG
     // Two groups of WAVES/2 waves (one wave per SIMD each), half a tile apart.
-    // Between consecutive barriers one group runs MFMAs (PV of tile t-1, then
-    // QK^T of tile t) while the other runs the softmax of its current tile, so
+    // Between consecutive barriers one group runs MFMAs (QK^T of tile t, then
+    // PV of tile t-1) while the other runs the softmax of its current tile, so
     // each SIMD's matrix core and vector ALU work at the same time.  K(t+1)
     // and V(t) are copied during iteration t and published by its final
     // barrier; a buffer is refilled only after the barrier that ends its last
@@ -403,8 +419,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // the one after the last tile (no QK^T, no copies) are shortened.
     // Copies.  Group 0's MFMA half of tile t (global phase 2t) copies K(t+1);
     // group 1's (phase 2t+1) copies V(t).  Both buffers' last readers
-    // finished in phase 2t-1, both tiles are awaited at the end of phase
-    // 2t+1, and neither is read before phase 2t+2.  Each wave issues its
+    // finished in phase 2t-1, each group awaits its copies at the end of its
+    // own MFMA half (K(t+1) is published at the end of phase 2t, V(t) at the
+    // end of phase 2t+1), and neither tile is read before phase 2t+2 -- except
+    // the first operands of the next MFMA stream, which each wave reads from
+    // K(t+1) at the end of its softmax half of tile t (phases 2t+1 and 2t+2),
+    // before the barrier, so that their LDS latency is not exposed at the
+    // start of the stream.  Each wave issues its
     // PER_G instructions one every kStep MFMA steps over the first half of its
     // stream, so no wave stalls on a full memory-request queue.  Everything
     // group-dependent is wave-uniform and selected, not branched on, so both
@@ -413,7 +434,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // others), and rows past the block re-read its last row.
     constexpr int kStep = (NT / 2) / PER_G;
     static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
-    auto mfma_half = [&]<bool PV, bool QK>(int t) __attribute__((always_inline)) {
+    auto mfma_half = [&]<bool PV, bool QK, bool PRE = false>(int t) __attribute__((always_inline)) {
         const bool gk = group == 0;
         const int tt = gk ? t + 1 : t;
         const int tc = min(tt, n_tiles - 1);
@@ -423,7 +444,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         const int last = kv_len - 1 - tc * kNk;  // last row of the block within tile tc
         const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
         if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        mfma_stream.template operator()<PV, QK>(t - 1, t, [&](int n) __attribute__((always_inline)) {
+        mfma_stream.template operator()<PV, QK, PRE>(t - 1, t, [&](int n) __attribute__((always_inline)) {
             if (QK && n % kStep == 0 && n / kStep < PER_G) {
                 const int i = n / kStep;
                 const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
@@ -445,34 +466,36 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // barrier (and group 0 one after its final PV half), so group 1 runs one
     // phase behind and both groups pass the same number of barriers.
     // Global phase 2t carries group 0's MFMA half of tile t and group 1's
-    // softmax half of tile t-1; phase 2t+1 the other way round.  The copies of
-    // K(t+1) and V(t) start in phase 2t (each group issues its share from the
-    // half that falls there) and are awaited at the end of phase 2t+1.
+    // softmax half of tile t-1; phase 2t+1 the other way round.
+    // barrier with no wait for outstanding LDS reads (the first operands of
+    // the next MFMA stream, read from a tile published one phase earlier); the
+    // memory clobber keeps the compiler from moving accesses across it
+    auto barrier = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
     if (n_tiles > 0) {
         issue_k(0);
         wait_vmem_all();
         __syncthreads();
-        if (group == 1) __syncthreads();
+        if (group == 1) barrier();
         // first tile: no PV product yet
         mfma_half.template operator()<false, true>(0);
-        if (group == 1) wait_vmem_all();
-        __syncthreads();
+        wait_vmem_all();
+        barrier();
         valu_half(0);
-        if (group == 0) wait_vmem_all();
-        __syncthreads();
+        if (1 < n_tiles) preload(1);
+        barrier();
         for (int t = 1; t < n_tiles; ++t) {
-            mfma_half.template operator()<true, true>(t);
-            if (group == 1) wait_vmem_all();
-            __syncthreads();
+            mfma_half.template operator()<true, true, true>(t);
+            wait_vmem_all();
+            barrier();
             valu_half(t);
-            if (group == 0) wait_vmem_all();
-            __syncthreads();
+            if (t + 1 < n_tiles) preload(t + 1);
+            barrier();
         }
         // PV product of the last tile (no copies).  Group 0 then passes the
         // barrier that ends group 1's last softmax half; group 1 runs its
         // final PV half with no barrier after it, while group 0 writes out.
         mfma_half.template operator()<true, false>(n_tiles);
-        if (group == 0) __syncthreads();
+        if (group == 0) barrier();
     }
 #else
     if (n_tiles > 0) {
