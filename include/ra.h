@@ -228,7 +228,14 @@ ra_status ra_ring_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * o: [n_run, batch, q_heads, Sb, head_dim] in dtype (normalised output)
  * lse: [n_run, batch, q_heads, Sb] binary32 (may be NULL)
  * All dense, position-major (the layout ra_stripe_permute produces).
- * workspace: device memory of at least ra_ring_workspace_size bytes.
+ * workspace: device memory of at least ra_ring_workspace_size bytes: the
+ * running states (fp32 O, m, l) of the run positions, partials, emulated
+ * transfer slots, and per library stream a block of tile-queue counters (the
+ * bf16 block kernel's workgroups claim query tiles from per-XCD queues and
+ * take over other XCDs' tiles once their own are done; the call zeroes the
+ * counters first and every launch leaves them zeroed).  Its contents need no
+ * initialisation; calls that may run at the same time need separate
+ * workspaces.
  * Concurrent calls are serialised on an internal mutex.
  * With stats == NULL the call only enqueues work -- kernel launches, event
  * records and waits (and, with emulate_copy, device-to-device copies) -- on

@@ -574,17 +574,38 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
     }
     wait_vmem_all();
 
-    // accumulator register v holds key c0w + 8(v/4) + 4 half + v%4, column d = 32 dblk + lane % 32
+    // accumulator register v holds key c0w + 8(v/4) + 4 half + v%4, column d = 32 dblk + lane % 32.
+    // The read-modify-write of dK and dV goes in two chunks of eight registers:
+    // every load of a chunk is issued before its first store, so each chunk
+    // costs one memory round trip.
     const int64_t kv0 = (static_cast<int64_t>(b) * a.Hkv + hk) * a.kv_len;
+    constexpr int VC = 8;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int c = c0w + 8 * (v / 4) + 4 * half + (v % 4);
-        if (c >= a.kv_len) continue;
+    for (int v0 = 0; v0 < 16; v0 += VC) {
+        float pk[VC][D / 32], pv[VC][D / 32];
 #pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
-            const int64_t o = (kv0 + c) * D + dblk * 32 + (lane & 31);
-            a.dk[o] = __builtin_fmaf(a.scale, dk[dblk][v], a.dk[o]);
-            a.dv[o] += dv[dblk][v];
+        for (int e = 0; e < VC; ++e) {
+            const int v = v0 + e, c = c0w + 8 * (v / 4) + 4 * half + (v % 4);
+            if (c < a.kv_len) {
+#pragma unroll
+                for (int dblk = 0; dblk < D / 32; ++dblk) {
+                    const int64_t o = (kv0 + c) * D + dblk * 32 + (lane & 31);
+                    pk[e][dblk] = a.dk[o];
+                    pv[e][dblk] = a.dv[o];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < VC; ++e) {
+            const int v = v0 + e, c = c0w + 8 * (v / 4) + 4 * half + (v % 4);
+            if (c < a.kv_len) {
+#pragma unroll
+                for (int dblk = 0; dblk < D / 32; ++dblk) {
+                    const int64_t o = (kv0 + c) * D + dblk * 32 + (lane & 31);
+                    a.dk[o] = __builtin_fmaf(a.scale, dk[dblk][v], pk[e][dblk]);
+                    a.dv[o] = pv[e][dblk] + dv[dblk][v];
+                }
+            }
         }
     }
 }

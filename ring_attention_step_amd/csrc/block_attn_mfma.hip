@@ -54,8 +54,12 @@
 // use.  Causal masking uses the block's mask offset: tiles past the
 // workgroup's last visible key are never loaded, and the element mask is
 // applied only on tiles that straddle the diagonal (or the ragged end of the
-// block).  Tiles are dispatched heaviest first and grouped so that one head's
-// workgroups land on the same XCD (shared L2 for K/V).
+// block).  Tiles are taken heaviest first and grouped so that one head's
+// tiles run on the same XCD (shared L2 for K/V); with work queues (the ring's
+// launches) one looping workgroup per compute unit claims them, and XCDs that
+// finish their share early take over the rest of the others'.
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "mfma_common.h"
@@ -129,9 +133,43 @@ __device__ inline float xhalf_sum(float x) {
 // Workgroup id -> logical tile id so that consecutive logical ids (one head's
 // query tiles) share an XCD: the dispatcher deals workgroups round-robin over
 // the 8 XCDs.  A bijection on [0, n).
-__device__ inline int64_t xcd_remap(int64_t w, int64_t n) {
-    const int64_t q = n / 8, r = n % 8, x = w % 8, i = w / 8;
+__device__ inline int xcd_remap(int w, int n) {
+    const int q = n / 8, r = n % 8, x = w % 8, i = w / 8;
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// Dynamic tile order.  The dispatcher deals workgroups to the 8 XCDs round
+// robin, so with one workgroup per tile every XCD runs the same share of
+// tiles whatever its speed, and a launch lasts as long as its slowest XCD
+// (measured: XCDs of one GPU differ by up to 13% in speed, so the fast ones
+// idle for the last few percent of every launch).  With work queues the
+// launch has one workgroup per compute unit, and each loops: it claims a
+// tile, processes it, claims the next.  XCD x's share (the logical ids
+// xcd_remap gives it, heaviest first) is a queue that its workgroups drain
+// in order, so a head's tiles still share one L2; a workgroup whose own queue
+// is empty takes the next tile of another XCD's queue (the lightest tiles
+// left there), and one that finds all 8 queues empty is done.  A failed
+// claim only ever finds a queue that stays empty, so one pass over the 8
+// queues decides, and no workgroup waits for another.  Counters live in
+// device memory (queue[0..7] the queue heads, queue[8] the number of
+// workgroups done claiming); they are updated with device-scope vector
+// atomics from one lane, and the last workgroup done claiming zeroes them for
+// the next launch (no workgroup of this launch reads them any more).
+__device__ inline int xcd_queue_start(int x, int n) {
+    const int q = n / 8, r = n % 8;
+    return x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+}
+// The next tile from this XCD's queue, else from another's; -1 when all are empty.
+__device__ inline int claim_tile(uint32_t* queue, int n) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    for (int k = 0; k < 8; ++k) {
+        const int x = static_cast<int>((xcc + k) & 7);
+        const uint32_t size = static_cast<uint32_t>(xcd_queue_start(x + 1, n) - xcd_queue_start(x, n));
+        const uint32_t i = __hip_atomic_fetch_add(queue + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < size) return xcd_queue_start(x, n) + static_cast<int>(i);
+    }
+    return -1;
 }
 
 // Two waves per SIMD (<= 256 registers): one wave's MFMAs overlap the other's
@@ -148,24 +186,43 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     __shared__ __attribute__((aligned(1024))) char smem[4 * TILE_BYTES];  // K0, K1, V0, V1
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qi = lane & 31;
-    const int half = lane >> 5;
 
     const int n_qt = (a.q_len + kMq - 1) / kMq;
-    const int64_t n_wg = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
+    const int n_wg = n_qt * a.Hq * a.B * a.n_splits;  // < 2^31 (the launch grid's limit; checked by the host)
     // (64-bit divisions expand to vector code: the results are made scalar
     // again, as the copy addresses need wave-uniform bases)
-    int64_t L = xcd_remap(blockIdx.x, n_wg);
-    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.n_splits));
-    L /= a.n_splits;
-    const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % n_qt));
-    L /= n_qt;
-    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % a.Hq));
-    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / a.Hq));
+    __shared__ int claimed;
+    for (;;) {  // one pass per tile: a single pass without work queues
+    int L;
+    if (a.queue) {
+        if (tid == 0) claimed = claim_tile(a.queue, n_wg);
+        __syncthreads();
+        const int c = __builtin_amdgcn_readfirstlane(claimed);
+        __syncthreads();  // every wave has read the claim before the next one is written
+        if (c < 0) break;
+        L = c;
+    } else {
+        L = xcd_remap(static_cast<int>(blockIdx.x), n_wg);
+    }
+    // the lane index, read afresh in every pass (volatile, so that nothing
+    // derived from it is kept live across passes, where registers are short)
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    const int qi = lane & 31;
+    const int half = lane >> 5;
+    // divisors as values of this pass (an empty volatile asm), so that the
+    // divisions' reciprocals are not kept live across passes
+    int d_split = a.n_splits, d_qt = n_qt, d_h = a.Hq, d_g = a.Hq / a.Hkv;
+    asm volatile("" : "+s"(d_split), "+s"(d_qt), "+s"(d_h), "+s"(d_g));
+    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_split));
+    L /= d_split;
+    const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_qt));
+    L /= d_qt;
+    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_h));
+    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / d_h));
     const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
-    const int hk = h / (a.Hq / a.Hkv);
+    const int hk = h / d_g;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
     // A key split sees keys [k_lo, k_lo + kv_len) of the block as a block of
     // its own: key c' of the split is key k_lo + c', so its mask offset is
@@ -530,31 +587,51 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         float m_out = m_true;  // log2 units
         float wa = 0.f, l_a = 0.f;
         float wp = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
+        f32x4* const dst = reinterpret_cast<f32x4*>(orow + 4 * half);  // + (8 dblk + 2 g) vectors
         if (a.accumulate) {
+            // every load of the running state is issued before the first store,
+            // so the row's read-modify-write costs one memory round trip
             const float m_a = mrow[idx] * kLog2e;  // -inf stays -inf
             l_a = lrow[idx];
+            f32x4 prev[D / 32][4];
+#pragma unroll
+            for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) prev[dblk][g] = dst[8 * dblk + 2 * g];
             m_out = fmaxf(m_a, m_true);
             wa = (m_a == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_a - m_out);
             wp = (m_true == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_out);
-        }
 #pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk) {
+            for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4* dst = reinterpret_cast<f32x4*>(orow + dblk * 32 + 8 * g + 4 * half);
-                f32x4 val = {oacc[dblk][4 * g] * wp, oacc[dblk][4 * g + 1] * wp, oacc[dblk][4 * g + 2] * wp,
-                             oacc[dblk][4 * g + 3] * wp};
-                if (a.accumulate) {
-                    const f32x4 prev = *dst;
-                    val = {__builtin_fmaf(wa, prev[0], val[0]), __builtin_fmaf(wa, prev[1], val[1]),
-                           __builtin_fmaf(wa, prev[2], val[2]), __builtin_fmaf(wa, prev[3], val[3])};
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 pv = prev[dblk][g];
+                    dst[8 * dblk + 2 * g] = f32x4{__builtin_fmaf(wa, pv[0], oacc[dblk][4 * g] * wp),
+                                                  __builtin_fmaf(wa, pv[1], oacc[dblk][4 * g + 1] * wp),
+                                                  __builtin_fmaf(wa, pv[2], oacc[dblk][4 * g + 2] * wp),
+                                                  __builtin_fmaf(wa, pv[3], oacc[dblk][4 * g + 3] * wp)};
                 }
-                *dst = val;
-            }
+        } else {
+#pragma unroll
+            for (int dblk = 0; dblk < D / 32; ++dblk)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    dst[8 * dblk + 2 * g] = f32x4{oacc[dblk][4 * g] * wp, oacc[dblk][4 * g + 1] * wp,
+                                                  oacc[dblk][4 * g + 2] * wp, oacc[dblk][4 * g + 3] * wp};
         }
         if (half == 0) {
             mrow[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
             lrow[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
+        }
+    }
+    if (!a.queue) break;
+    }  // tile loop
+    if (a.queue && tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(a.queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == gridDim.x - 1) {
+#pragma unroll
+            for (int x = 0; x < 9; ++x)
+                __hip_atomic_exchange(a.queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -562,6 +639,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kWaves = RA_MFMA_WAVES;
+
+// Compute units of the current device (cached per device id).
+int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 }  // namespace
 
@@ -581,7 +671,9 @@ hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s) {
     constexpr int kMq = 32 * kWaves;
     const int n_qt = (a.q_len + kMq - 1) / kMq;
     if (a.n_splits < 1 || (a.n_splits > 1 && (a.accumulate || a.split_tiles < 1))) return hipErrorInvalidValue;
-    const int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
+    int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;  // tile ids are 32-bit
+    if (a.queue) blocks = std::min<int64_t>(blocks, compute_units());  // one looping workgroup per CU
     if (a.D == 128)
         hipLaunchKernelGGL((block_mfma_kernel<128, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
                            0, s, a);

@@ -232,6 +232,7 @@ struct RingGeometry {
     int32_t n_splits, split_tiles;  // key splits of every block launch (1: none)
     int32_t n_part;                 // partials per stream (0, 1 or n_splits)
     size_t acc_o, acc_ml, part_o, part_ml, slot;  // bytes, each 256-aligned
+    size_t queue;                                 // per stream: the block kernel's tile-queue counters
     size_t total;
 };
 
@@ -296,9 +297,11 @@ RingGeometry geometry(const ra_ring_desc* d) {
     g.part_o = g.n_part ? g.acc_o : 0;
     g.part_ml = g.n_part ? g.acc_ml : 0;
     g.slot = d->emulate_copy ? round_up(static_cast<size_t>(g.kv_elems) * elem_size(d->dtype), 256) : 0;
-    // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: n_part partials o, m, l
+    g.queue = round_up(ra::kQueueWords * sizeof(uint32_t), 256);
+    // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: n_part
+    // partials o, m, l and the tile-queue counters of its block launches
     g.total = static_cast<size_t>(d->n_run) * (g.acc_o + 2 * g.acc_ml + 4 * g.slot) +
-              static_cast<size_t>(g.n_streams) * g.n_part * (g.part_o + 2 * g.part_ml);
+              static_cast<size_t>(g.n_streams) * (g.n_part * (g.part_o + 2 * g.part_ml) + g.queue);
     return g;
 }
 
@@ -418,6 +421,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     }
     struct StreamBufs {
         float *o, *m, *l;
+        uint32_t* queue;
     };
     std::vector<StreamBufs> part(g.n_streams);  // partial i at o + i part_o, m / l + i part_ml
     for (int s = 0; s < g.n_streams; ++s) {
@@ -427,6 +431,8 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         ws += g.n_part * g.part_ml;
         part[s].l = reinterpret_cast<float*>(ws);
         ws += g.n_part * g.part_ml;
+        part[s].queue = reinterpret_cast<uint32_t*>(ws);
+        ws += g.queue;
     }
 
     std::vector<std::vector<RingPlanStep>> plan(d->n_run);
@@ -469,6 +475,12 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     for (int s = 0; s < g.n_streams; ++s) {
         RA_HIP(hipStreamWaitEvent(ds.compute[s], ev_fork, 0));
         if (d->emulate_copy) RA_HIP(hipStreamWaitEvent(ds.copy[s], ev_fork, 0));
+        // the stream's tile-queue counters start at zero (each block launch
+        // leaves them so); a fill kernel, not a memset, so that the call can be
+        // captured in a graph
+        const hipError_t e = ra::launch_fill_zero(reinterpret_cast<float*>(part[s].queue),
+                                                  static_cast<int64_t>(g.queue / 4), ds.compute[s]);
+        if (e != hipSuccess) return hip_fail(e, "queue reset launch");
     }
 
     const char* kb = static_cast<const char*>(k);
@@ -543,6 +555,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                 a.scale = resolve_scale(d->scale, D);
                 a.causal = d->causal;
                 a.mask_offset = clamp_offset(ps.offset, Sb, Sb);
+                a.queue = part[sid].queue;  // launches on one stream run one after another
                 const bool split = g.n_splits > 1 && ra::mfma_eligible(a, d->dtype);
                 if (split) {  // the block's key ranges as partials, folded by the merge below
                     stats.kv_splits = g.n_splits;

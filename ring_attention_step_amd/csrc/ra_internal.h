@@ -33,7 +33,14 @@ struct BlockArgs {
     int32_t n_splits = 1;
     int32_t split_tiles = 0;
     int64_t part_o_stride = 0, part_ml_stride = 0;
+    // Work queues (MFMA kernel only): NULL keeps the fixed workgroup -> tile
+    // order.  Otherwise kQueueWords zeroed counters in device memory: each
+    // workgroup claims its tile from its XCD's queue (heaviest first) and,
+    // once that queue is empty, from the others; the launch leaves them zeroed.
+    // Launches that may run at the same time need counters of their own.
+    uint32_t* queue = nullptr;
 };
+constexpr int kQueueWords = 16;  // 8 per-XCD queue heads, the claim count, padding
 
 // Vector-ALU kernel: binary32 or bfloat16 inputs, any D in [1, 256], fp32 math.
 hipError_t launch_block_simt(const BlockArgs& a, int dtype, hipStream_t s);

@@ -157,19 +157,23 @@ def _ring_desc(**kw):
     return d
 
 
+QUEUE = 256  # bytes of tile-queue counters per stream of a ring call
+
+
 def test_ring_workspace_and_validation(lib):
     n = ctypes.c_size_t()
     d = _ring_desc()
     assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
     rows = 32 * 32768
-    # fused schedule: one running state (fp32 O, m, l) per computed position
-    assert n.value == rows * 128 * 4 + 2 * rows * 4
+    # fused schedule: one running state (fp32 O, m, l) per computed position,
+    # and one 256-byte block of tile-queue counters per stream (one stream here)
+    assert n.value == rows * 128 * 4 + 2 * rows * 4 + QUEUE
     s = _ring_desc(separate_merge=1)  # plus one partial per stream
     assert lib.ra_ring_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.RA_OK
-    assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4)
+    assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4) + QUEUE
     e = _ring_desc(emulate_copy=1)
     assert lib.ra_ring_workspace_size(ctypes.byref(e), ctypes.byref(n)) == B.RA_OK
-    assert n.value == (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2)
+    assert n.value == (rows * 128 * 4 + 2 * rows * 4) + 4 * (8 * 32768 * 128 * 2) + QUEUE
     for kw in ({"first_pos": 32}, {"n_run": 2}, {"layout": 3}, {"n_pos": 0}, {"block_len": 0},
                {"emulate_copy": 2}, {"kv_heads": 5}, {"n_streams": -1}, {"separate_merge": 2},
                {"kv_splits": -1}, {"kv_splits": 9}):
@@ -198,7 +202,8 @@ def test_kv_split_workspace(lib):
     def size(**extra):
         d = _ring_desc(**kw, **extra)
         assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
-        return n.value
+        streams = extra.get("n_streams", 2)
+        return n.value - streams * QUEUE  # the partials and running states alone
 
     assert size(kv_splits=1) == 2 * state
     assert size() == 2 * state + 2 * 4 * state  # automatic: 4 ranges of 4 tiles

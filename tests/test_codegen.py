@@ -60,7 +60,7 @@ def test_mfma_kernel_registers_scratch_and_m0(tmp_path, src, pattern, count):
         for line in body.splitlines():
             code = line.split(";")[0]
             if re.search(r"\bm0\b", code):
-                assert re.match(r"\s*s_mov_b32 m0, s\d+\s*$", code), f"{name}: unexpected m0 use: {code.strip()}"
+                assert re.match(r"\s*s_mov_b32 m0, (?:s\d+|vcc_lo|vcc_hi)\s*$", code), f"{name}: unexpected m0 use: {code.strip()}"
     # resource metadata: scratch (private segment) size and VGPR count per kernel
     for name in kernels:
         at = asm.find(f".name:           {name}")
