@@ -155,23 +155,6 @@ __device__ inline int xcd_remap(int w, int n) {
 // workgroups done claiming); they are updated with device-scope vector
 // atomics from one lane, and the last workgroup done claiming zeroes them for
 // the next launch (no workgroup of this launch reads them any more).
-__device__ inline int xcd_queue_start(int x, int n) {
-    const int q = n / 8, r = n % 8;
-    return x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-}
-// The next tile from this XCD's queue, else from another's; -1 when all are empty.
-__device__ inline int claim_tile(uint32_t* queue, int n) {
-    uint32_t xcc;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-    for (int k = 0; k < 8; ++k) {
-        const int x = static_cast<int>((xcc + k) & 7);
-        const uint32_t size = static_cast<uint32_t>(xcd_queue_start(x + 1, n) - xcd_queue_start(x, n));
-        const uint32_t i = __hip_atomic_fetch_add(queue + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (i < size) return xcd_queue_start(x, n) + static_cast<int>(i);
-    }
-    return -1;
-}
-
 // Two waves per SIMD (<= 256 registers): one wave's MFMAs overlap the other's
 // softmax arithmetic.
 template <int D, int WAVES>
@@ -626,19 +609,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     if (!a.queue) break;
     }  // tile loop
-    if (a.queue && tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(a.queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1) {
-#pragma unroll
-            for (int x = 0; x < 9; ++x)
-                __hip_atomic_exchange(a.queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (a.queue && tid == 0) finish_claims(a.queue, gridDim.x);
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kWaves = RA_MFMA_WAVES;
+
+}  // namespace
 
 // Compute units of the current device (cached per device id).
 int compute_units() {
@@ -653,7 +631,6 @@ int compute_units() {
     return n;
 }
 
-}  // namespace
 
 bool mfma_eligible(const BlockArgs& a, int dtype) {
     if (dtype != 1 || (a.D != 64 && a.D != 128)) return false;

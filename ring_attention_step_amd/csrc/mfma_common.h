@@ -90,5 +90,35 @@ __device__ inline void lds_dma4(const void* base, uint32_t offset, uint32_t lds_
         : "memory", "m0");
 }
 
+// Work queues of persistent workgroups (see block_attn_mfma.hip): a tile
+// space of n logical ids is cut into 8 queues, queue x holding the ids the
+// fixed order places on XCD x; queue[0..7] are the queue heads, queue[8] the
+// number of workgroups done claiming.
+__device__ inline int xcd_queue_start(int x, int n) {
+    const int q = n / 8, r = n % 8;
+    return x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+}
+// The next tile from this XCD's queue, else from another's; -1 when all are empty.
+__device__ inline int claim_tile(uint32_t* queue, int n) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    for (int k = 0; k < 8; ++k) {
+        const int x = static_cast<int>((xcc + k) & 7);
+        const uint32_t size = static_cast<uint32_t>(xcd_queue_start(x + 1, n) - xcd_queue_start(x, n));
+        const uint32_t i = __hip_atomic_fetch_add(queue + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (i < size) return xcd_queue_start(x, n) + static_cast<int>(i);
+    }
+    return -1;
+}
+// Called once per workgroup (one lane) after its last, failed claim: the last
+// workgroup of the grid zeroes the counters for the next launch.
+__device__ inline void finish_claims(uint32_t* queue, uint32_t n_workgroups) {
+    const uint32_t done = __hip_atomic_fetch_add(queue + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == n_workgroups - 1) {
+#pragma unroll
+        for (int x = 0; x < 9; ++x) __hip_atomic_exchange(queue + x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 }  // namespace mfma
 }  // namespace ra

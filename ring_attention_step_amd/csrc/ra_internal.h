@@ -41,6 +41,8 @@ struct BlockArgs {
     uint32_t* queue = nullptr;
 };
 constexpr int kQueueWords = 16;  // 8 per-XCD queue heads, the claim count, padding
+// Compute units of the current device (one persistent workgroup each).
+int compute_units();
 
 // Vector-ALU kernel: binary32 or bfloat16 inputs, any D in [1, 256], fp32 math.
 hipError_t launch_block_simt(const BlockArgs& a, int dtype, hipStream_t s);
