@@ -471,6 +471,14 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     Timer timer;
     if (d->stats) timer.pool = &ds.timing_events;
 
+    // Work queues pay off when a block launch has many more query tiles than
+    // the GPU has compute units (each workgroup then loops over several and
+    // the XCDs can even out); a launch with fewer tiles keeps one workgroup
+    // per tile in the fixed order, as the claims would only add latency.
+    const int64_t launch_tiles = (Sb + ra::mfma_query_tile() - 1) / ra::mfma_query_tile() * d->q_heads *
+                                 d->batch * g.n_splits;
+    const bool use_queue = launch_tiles >= 2 * static_cast<int64_t>(ra::compute_units());
+
     RA_HIP(hipEventRecord(ev_fork, caller));
     for (int s = 0; s < g.n_streams; ++s) {
         RA_HIP(hipStreamWaitEvent(ds.compute[s], ev_fork, 0));
@@ -478,9 +486,11 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         // the stream's tile-queue counters start at zero (each block launch
         // leaves them so); a fill kernel, not a memset, so that the call can be
         // captured in a graph
-        const hipError_t e = ra::launch_fill_zero(reinterpret_cast<float*>(part[s].queue),
-                                                  static_cast<int64_t>(g.queue / 4), ds.compute[s]);
-        if (e != hipSuccess) return hip_fail(e, "queue reset launch");
+        if (use_queue) {
+            const hipError_t e = ra::launch_fill_zero(reinterpret_cast<float*>(part[s].queue),
+                                                      static_cast<int64_t>(g.queue / 4), ds.compute[s]);
+            if (e != hipSuccess) return hip_fail(e, "queue reset launch");
+        }
     }
 
     const char* kb = static_cast<const char*>(k);
@@ -555,7 +565,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                 a.scale = resolve_scale(d->scale, D);
                 a.causal = d->causal;
                 a.mask_offset = clamp_offset(ps.offset, Sb, Sb);
-                a.queue = part[sid].queue;  // launches on one stream run one after another
+                a.queue = use_queue ? part[sid].queue : nullptr;  // launches on one stream run in turn
                 const bool split = g.n_splits > 1 && ra::mfma_eligible(a, d->dtype);
                 if (split) {  // the block's key ranges as partials, folded by the merge below
                     stats.kv_splits = g.n_splits;
