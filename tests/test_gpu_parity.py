@@ -446,3 +446,45 @@ def test_ring_forward_graph_replay(splits):
     hh, tt = np.meshgrid(np.arange(H), np.arange(S), indexing="ij")
     sel = np.arange(0, H * S, 37)
     gh.compare_rows(o_sh, lse, qn, kn, vn, hh.ravel()[sel], tt.ravel()[sel], N, "contiguous", 0, False, "bf16")
+
+
+@pytest.mark.parametrize("lay", ["striped", "contiguous"])
+def test_work_queue_ring_equals_fixed_order_blocks(lay):
+    """A ring whose block launches have many more query tiles than the GPU has
+    compute units runs them through the kernel's work queues (persistent
+    workgroups claiming tiles from per-XCD queues).  The same fused schedule
+    composed from ra_block_attn_fwd calls (one workgroup per tile, fixed
+    order) and a finalising ra_lse_merge must give bit-identical O and lse:
+    every tile is then processed exactly once by the queues, with the same
+    arithmetic, in every step of the ring (the counters each launch leaves for
+    the next included)."""
+    B, Hq, Hkv, D, N = 1, 32, 8, 128, 4
+    Sb = max(4096, 2 * torch.cuda.get_device_properties(0).multi_processor_count * 256 // Hq)
+    S, i = Sb * N, N - 1
+    gh.say("ra_ring_forward work queues vs fixed-order blocks", lay, Sb)
+    qn, kn, vn = gh.qkv_global(B, Hq, Hkv, S, D, "bf16", seed=41)
+    qs, ks, vs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn))
+    del qn, kn, vn
+    q_run = qs[i:i + 1].contiguous()
+    o_ring, lse_ring, _ = gh.run_ring(q_run, ks, vs, N, i, lay, True)
+
+    o = torch.empty(B, Hq, Sb, D, device="cuda")
+    m = torch.empty(B, Hq, Sb, device="cuda")
+    l = torch.empty_like(m)
+    for s in range(N):
+        j = (i - s) % N
+        if lay == "striped":  # token i + N r of position i, j + N c of block j
+            pos = dict(q_pos0=i, k_pos0=j, pos_stride=N)
+        else:
+            pos = dict(q_pos0=i * Sb, k_pos0=j * Sb, pos_stride=1)
+        if lay == "contiguous" and j > i:
+            continue  # fully masked: the ring skips it too
+        first = s == 0
+        ra.ra_block_attn_fwd(q_run[0], ks[j], vs[j], o, m, l, causal=True,
+                             flags=0 if first else ra.RA_BLOCK_ACCUMULATE, **pos)
+    o_blk = torch.empty(B, Hq, Sb, D, dtype=torch.bfloat16, device="cuda")
+    lse_blk = torch.empty(B, Hq, Sb, device="cuda")
+    ra.ra_lse_merge(o, m, l, o_out=o_blk, lse_out=lse_blk)
+    torch.cuda.synchronize()
+    assert torch.equal(o_ring[0].view(torch.int16), o_blk.view(torch.int16))
+    assert torch.equal(lse_ring[0], lse_blk)
