@@ -400,13 +400,17 @@ def test_kv_split_ring_matches_oracle(lay, causal, D, Sb, N, splits, used):
     assert torch.equal(o3, o1) and torch.equal(l3, l1)
 
 
-@pytest.mark.parametrize("splits", [0, 1])
-def test_ring_forward_graph_replay(splits):
+@pytest.mark.parametrize("H,S,D,splits", [(4, 4096, 64, 0), (4, 4096, 64, 1), (32, 8192, 128, 0)],
+                         ids=["key-splits", "no-splits", "work-queues"])
+def test_ring_forward_graph_replay(H, S, D, splits):
     """A whole ring step (permute in, ra_ring_forward, permute out) captured
     into a HIP graph: every replay, with eager work and synchronisations
-    between replays, reproduces the eager step bit for bit."""
-    B, H, S, D, N = 1, 4, 4096, 64, 2
-    gh.say("ra_ring_forward graph replay", splits)
+    between replays, reproduces the eager step bit for bit.  The small ring
+    runs with key splits or without; the larger one (512 query tiles a
+    launch) takes the block kernel's work queues, whose counters the call
+    zeroes with a fill kernel and every launch leaves zeroed."""
+    B, N = 1, 2
+    gh.say("ra_ring_forward graph replay", H, S, D, splits)
     qn, kn, vn = gh.qkv_global(B, H, H, S, D, "bf16", seed=3)
     q_g, k_g, v_g = (gh.to_device(x, "bf16") for x in (qn, kn, vn))
     q_sh = torch.empty((N, B, H, S // N, D), dtype=torch.bfloat16, device="cuda")
