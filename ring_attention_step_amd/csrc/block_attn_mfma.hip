@@ -130,9 +130,13 @@ __device__ inline float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup id -> logical tile id so that consecutive logical ids (one head's
-// query tiles) share an XCD: the dispatcher deals workgroups round-robin over
-// the 8 XCDs.  A bijection on [0, n).
+// Workgroup id -> logical tile id so that consecutive logical ids share an
+// XCD: the dispatcher deals workgroups round-robin over the 8 XCDs.  A
+// bijection on [0, n).  XCD x gets the logical ids [start(x), start(x + 1));
+// when those are whole heads (hpx = Hq B / 8 of them, no key splits) they are
+// ordered query tile first, head second, so that each XCD's share (one KV
+// head's group under GQA, sharing its K/V in L2) runs heaviest first as a
+// whole; otherwise head by head.
 __device__ inline int xcd_remap(int w, int n) {
     const int q = n / 8, r = n % 8, x = w % 8, i = w / 8;
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
@@ -198,12 +202,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // divisions' reciprocals are not kept live across passes
     int d_split = a.n_splits, d_qt = n_qt, d_h = a.Hq, d_g = a.Hq / a.Hkv;
     asm volatile("" : "+s"(d_split), "+s"(d_qt), "+s"(d_h), "+s"(d_g));
-    const int split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_split));
-    L /= d_split;
-    const int qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_qt));
-    L /= d_qt;
-    const int h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_h));
-    const int b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / d_h));
+    int split, qt_rank, h, b;
+    if (a.n_splits == 1 && (a.Hq * a.B) % 8 == 0) {
+        // every XCD's share is whole heads (hpx of them): order it query tile
+        // first, head second, so that the share runs heaviest first as a whole
+        int d_hpx = a.Hq * a.B / 8;
+        asm volatile("" : "+s"(d_hpx));
+        const int x = L / (d_qt * d_hpx), i = L - x * (d_qt * d_hpx);
+        const int hb = x * d_hpx + i % d_hpx;
+        split = 0;
+        qt_rank = __builtin_amdgcn_readfirstlane(i / d_hpx);
+        h = __builtin_amdgcn_readfirstlane(hb % d_h);
+        b = __builtin_amdgcn_readfirstlane(hb / d_h);
+    } else {
+        split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_split));
+        L /= d_split;
+        qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_qt));
+        L /= d_qt;
+        h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_h));
+        b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / d_h));
+    }
     const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
     const int hk = h / d_g;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
