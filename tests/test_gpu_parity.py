@@ -452,8 +452,9 @@ def test_ring_forward_graph_replay(H, S, D, splits):
     gh.compare_rows(o_sh, lse, qn, kn, vn, hh.ravel()[sel], tt.ravel()[sel], N, "contiguous", 0, False, "bf16")
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("lay", ["striped", "contiguous"])
-def test_work_queue_ring_equals_fixed_order_blocks(lay):
+def test_work_queue_ring_equals_fixed_order_blocks(lay, D):
     """A ring whose block launches have many more query tiles than the GPU has
     compute units runs them through the kernel's work queues (persistent
     workgroups claiming tiles from per-XCD queues).  The same fused schedule
@@ -462,10 +463,10 @@ def test_work_queue_ring_equals_fixed_order_blocks(lay):
     every tile is then processed exactly once by the queues, with the same
     arithmetic, in every step of the ring (the counters each launch leaves for
     the next included)."""
-    B, Hq, Hkv, D, N = 1, 32, 8, 128, 4
+    B, Hq, Hkv, N = 1, 32, 8, 4
     Sb = max(4096, 2 * torch.cuda.get_device_properties(0).multi_processor_count * 256 // Hq)
     S, i = Sb * N, N - 1
-    gh.say("ra_ring_forward work queues vs fixed-order blocks", lay, Sb)
+    gh.say("ra_ring_forward work queues vs fixed-order blocks", lay, D, Sb)
     qn, kn, vn = gh.qkv_global(B, Hq, Hkv, S, D, "bf16", seed=41)
     qs, ks, vs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn))
     del qn, kn, vn
