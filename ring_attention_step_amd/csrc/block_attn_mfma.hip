@@ -181,451 +181,455 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
     // again, as the copy addresses need wave-uniform bases)
     __shared__ int claimed;
     for (;;) {  // one pass per tile: a single pass without work queues
-    int L;
-    if (a.queue) {
-        if (tid == 0) claimed = claim_tile(a.queue, n_wg);
-        __syncthreads();
-        const int c = __builtin_amdgcn_readfirstlane(claimed);
-        __syncthreads();  // every wave has read the claim before the next one is written
-        if (c < 0) break;
-        L = c;
-    } else {
-        L = xcd_remap(static_cast<int>(blockIdx.x), n_wg);
-    }
-    // the lane index, read afresh in every pass (volatile, so that nothing
-    // derived from it is kept live across passes, where registers are short)
-    int lane;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
-    const int qi = lane & 31;
-    const int half = lane >> 5;
-    // divisors as values of this pass (an empty volatile asm), so that the
-    // divisions' reciprocals are not kept live across passes
-    int d_split = a.n_splits, d_qt = n_qt, d_h = a.Hq, d_g = a.Hq / a.Hkv;
-    asm volatile("" : "+s"(d_split), "+s"(d_qt), "+s"(d_h), "+s"(d_g));
-    int split, qt_rank, h, b;
-    if (a.n_splits == 1 && (a.Hq * a.B) % 8 == 0) {
-        // every XCD's share is whole heads (hpx of them): order it query tile
-        // first, head second, so that the share runs heaviest first as a whole
-        int d_hpx = a.Hq * a.B / 8;
-        asm volatile("" : "+s"(d_hpx));
-        const int x = L / (d_qt * d_hpx), i = L - x * (d_qt * d_hpx);
-        const int hb = x * d_hpx + i % d_hpx;
-        split = 0;
-        qt_rank = __builtin_amdgcn_readfirstlane(i / d_hpx);
-        h = __builtin_amdgcn_readfirstlane(hb % d_h);
-        b = __builtin_amdgcn_readfirstlane(hb / d_h);
-    } else {
-        split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_split));
-        L /= d_split;
-        qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_qt));
-        L /= d_qt;
-        h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_h));
-        b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / d_h));
-    }
-    const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
-    const int hk = h / d_g;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
-    // A key split sees keys [k_lo, k_lo + kv_len) of the block as a block of
-    // its own: key c' of the split is key k_lo + c', so its mask offset is
-    // mask_offset - k_lo.
-    const int k_lo = split * a.split_tiles * kNk;
-    const int kv_len = a.n_splits > 1 ? max(0, min(a.kv_len - k_lo, a.split_tiles * kNk)) : a.kv_len;
-    const int mask_offset = a.mask_offset - k_lo;
-    const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1] + k_lo * a.ks[2];
-    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1] + k_lo * a.vs[2];
-
-    const int r0 = qt * kMq;
-    const int q0w = r0 + wave * 32;  // first query row of this wave
-    const int row = q0w + qi;        // this lane's query row
-
-    // Q as the B operand: 8 consecutive head_dim elements of this lane's row.
-    bf16x8 qreg[D / 16];
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) {
-        if (row < a.q_len)
-            qreg[kb] = *reinterpret_cast<const bf16x8*>(qp + row * a.qs[2] + kb * 16 + half * 8);
-        else
-            qreg[kb] = bf16x8{};
-    }
-
-    int key_end = kv_len;
-    if (a.causal) key_end = min(key_end, min(a.q_len - 1, r0 + kMq - 1) + mask_offset + 1);
-    const int n_tiles = key_end > 0 ? (key_end + kNk - 1) / kNk : 0;
-
-    // keys this wave may see, and keys every row of this wave sees
-    int wave_key_end = 0, wave_full_end = 0;
-    if (q0w < a.q_len) {
-        wave_key_end = kv_len;
-        wave_full_end = kv_len;
-        if (a.causal) {
-            wave_key_end = min(kv_len, min(a.q_len - 1, q0w + 31) + mask_offset + 1);
-            wave_full_end = max(0, min(kv_len, q0w + mask_offset + 1));
+        int L;
+        if (a.queue) {
+            if (tid == 0) claimed = claim_tile(a.queue, n_wg);
+            __syncthreads();
+            const int c = __builtin_amdgcn_readfirstlane(claimed);
+            __syncthreads();  // every wave has read the claim before the next one is written
+            if (c < 0) break;
+            L = c;
+        } else {
+            L = xcd_remap(static_cast<int>(blockIdx.x), n_wg);
         }
-    }
+        // the lane index, read afresh in every pass (volatile, so that nothing
+        // derived from it is kept live across passes, where registers are short)
+        int lane;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+        const int qi = lane & 31;
+        const int half = lane >> 5;
+        // divisors as values of this pass (an empty volatile asm), so that the
+        // divisions' reciprocals are not kept live across passes
+        int d_split = a.n_splits, d_qt = n_qt, d_h = a.Hq, d_g = a.Hq / a.Hkv;
+        asm volatile("" : "+s"(d_split), "+s"(d_qt), "+s"(d_h), "+s"(d_g));
+        int split, qt_rank, h, b;
+        if (a.n_splits == 1 && (a.Hq * a.B) % 8 == 0) {
+            // every XCD's share is whole heads (hpx of them): order it query tile
+            // first, head second, so that the share runs heaviest first as a whole
+            int d_hpx = a.Hq * a.B / 8;
+            asm volatile("" : "+s"(d_hpx));
+            const int x = L / (d_qt * d_hpx), i = L - x * (d_qt * d_hpx);
+            const int hb = x * d_hpx + i % d_hpx;
+            split = 0;
+            qt_rank = __builtin_amdgcn_readfirstlane(i / d_hpx);
+            h = __builtin_amdgcn_readfirstlane(hb % d_h);
+            b = __builtin_amdgcn_readfirstlane(hb / d_h);
+        } else {
+            split = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_split));
+            L /= d_split;
+            qt_rank = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_qt));
+            L /= d_qt;
+            h = __builtin_amdgcn_readfirstlane(static_cast<int>(L % d_h));
+            b = __builtin_amdgcn_readfirstlane(static_cast<int>(L / d_h));
+        }
+        const int qt = a.causal ? (n_qt - 1 - qt_rank) : qt_rank;  // heaviest first
+        const int hk = h / d_g;
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + b * a.qs[0] + h * a.qs[1];
+        // A key split sees keys [k_lo, k_lo + kv_len) of the block as a block of
+        // its own: key c' of the split is key k_lo + c', so its mask offset is
+        // mask_offset - k_lo.
+        const int k_lo = split * a.split_tiles * kNk;
+        const int kv_len = a.n_splits > 1 ? max(0, min(a.kv_len - k_lo, a.split_tiles * kNk)) : a.kv_len;
+        const int mask_offset = a.mask_offset - k_lo;
+        const uint16_t* kp = static_cast<const uint16_t*>(a.k) + b * a.ks[0] + hk * a.ks[1] + k_lo * a.ks[2];
+        const uint16_t* vp = static_cast<const uint16_t*>(a.v) + b * a.vs[0] + hk * a.vs[1] + k_lo * a.vs[2];
 
-    // Tile copies.  K tiles live in LDS buffers 0/1, V tiles in buffers 2/3.
-    // Instruction i of this wave fills chunk positions [64 i', 64 i' + 64) of a
-    // tile (i' = wave-major instruction index); each lane fetches the global
-    // chunk that belongs at its position.  Rows past the block re-read its last
-    // row (finite values; they are masked).
-    const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
-    // per-lane byte offsets of this wave's copy instructions within a full tile
-    uint32_t kcp[PER_WAVE], vcp[PER_WAVE];
-    int crow[PER_WAVE], cchunk[PER_WAVE];
+        const int r0 = qt * kMq;
+        const int q0w = r0 + wave * 32;  // first query row of this wave
+        const int row = q0w + qi;        // this lane's query row
+
+        // Q as the B operand: 8 consecutive head_dim elements of this lane's row.
+        bf16x8 qreg[D / 16];
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-        const int pos = (wave * PER_WAVE + i) * 64 + lane;
-        crow[i] = pos / CPR;
-        cchunk[i] = (pos % CPR) ^ swz<D>(crow[i]);
-        kcp[i] = static_cast<uint32_t>(crow[i] * ks2 * 2 + cchunk[i] * 16);
-        vcp[i] = static_cast<uint32_t>(crow[i] * vs2 * 2 + cchunk[i] * 16);
-    }
-    auto issue_copy = [&](const uint16_t* src, int64_t stride, const uint32_t* off, int t, int buf)
-                          __attribute__((always_inline)) {
-        const uint16_t* base = src + static_cast<int64_t>(t) * kNk * stride;
-        const uint32_t dst = lds0 + buf * TILE_BYTES;
-        const int last = kv_len - 1 - t * kNk;  // last valid row of this tile
-        if (last >= kNk - 1) {
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) lds_dma16(base, off[i], dst + (wave * PER_WAVE + i) * 1024);
-        } else {  // ragged end of the block: rows past it re-read its last row (masked later)
-#pragma unroll
-            for (int i = 0; i < PER_WAVE; ++i) {
-                const uint32_t o = static_cast<uint32_t>(min(crow[i], last) * stride * 2 + cchunk[i] * 16);
-                lds_dma16(base, o, dst + (wave * PER_WAVE + i) * 1024);
+        for (int kb = 0; kb < D / 16; ++kb) {
+            if (row < a.q_len)
+                qreg[kb] = *reinterpret_cast<const bf16x8*>(qp + row * a.qs[2] + kb * 16 + half * 8);
+            else
+                qreg[kb] = bf16x8{};
+        }
+
+        int key_end = kv_len;
+        if (a.causal) key_end = min(key_end, min(a.q_len - 1, r0 + kMq - 1) + mask_offset + 1);
+        const int n_tiles = key_end > 0 ? (key_end + kNk - 1) / kNk : 0;
+
+        // keys this wave may see, and keys every row of this wave sees
+        int wave_key_end = 0, wave_full_end = 0;
+        if (q0w < a.q_len) {
+            wave_key_end = kv_len;
+            wave_full_end = kv_len;
+            if (a.causal) {
+                wave_key_end = min(kv_len, min(a.q_len - 1, q0w + 31) + mask_offset + 1);
+                wave_full_end = max(0, min(kv_len, q0w + mask_offset + 1));
             }
         }
-    };
-    auto issue_k = [&](int t) __attribute__((always_inline)) { issue_copy(kp, ks2, kcp, t, t & 1); };
-    auto issue_v = [&](int t) __attribute__((always_inline)) { issue_copy(vp, vs2, vcp, t, 2 + (t & 1)); };
-    // Ping-pong copies: group 0 copies K tiles, group 1 V tiles, each group's
-    // four waves one instruction at a time from inside their MFMA stream.
-    // Instruction i of wave slot w (w = wave mod WAVES/2) fills chunk
-    // positions [64 (w PER_G + i), +64) of the tile: rows crow0 + RPI i.
-    constexpr int PER_G = INSTR / (WAVES / 2);  // copy instructions per wave per tile
-    constexpr int RPI = 64 / CPR;               // tile rows per copy instruction
-    static_assert(INSTR % (WAVES / 2) == 0, "tile copy must split evenly over a wave group");
-    const int wslot = wave % (WAVES / 2);
-    const int crow0 = wslot * PER_G * RPI + lane / CPR;
-    uint32_t cc16[PER_G];
-#pragma unroll
-    for (int i = 0; i < PER_G; ++i) cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
 
-    // per-lane LDS byte offsets of the operand reads
-    const lds_char* lds = RA_LDS_PTR(char, smem);
-    const int sq = swz<D>(qi);  // K rows sub*32 + qi share swz(qi)
-    uint32_t koff[D / 16];
+        // Tile copies.  K tiles live in LDS buffers 0/1, V tiles in buffers 2/3.
+        // Instruction i of this wave fills chunk positions [64 i', 64 i' + 64) of a
+        // tile (i' = wave-major instruction index); each lane fetches the global
+        // chunk that belongs at its position.  Rows past the block re-read its last
+        // row (finite values; they are masked).
+        const int64_t ks2 = a.ks[2], vs2 = a.vs[2];
+        const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
+        // per-lane byte offsets of this wave's copy instructions within a full tile
+        uint32_t kcp[PER_WAVE], vcp[PER_WAVE];
+        int crow[PER_WAVE], cchunk[PER_WAVE];
 #pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) koff[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
-    const int j = lane & 15;                        // lane within its 16-lane group
-    const int dsub = (lane >> 4) & 1;               // which 16 columns of a 32-column block
-    const int vrow = 4 * half + (j >> 2);           // row within a 16-row k-block (first run)
-    const int sv_lo = swz<D>(vrow), sv_hi = swz<D>(vrow + 8);
-    uint32_t voff_lo[D / 32], voff_hi[D / 32];
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int pos = (wave * PER_WAVE + i) * 64 + lane;
+            crow[i] = pos / CPR;
+            cchunk[i] = (pos % CPR) ^ swz<D>(crow[i]);
+            kcp[i] = static_cast<uint32_t>(crow[i] * ks2 * 2 + cchunk[i] * 16);
+            vcp[i] = static_cast<uint32_t>(crow[i] * vs2 * 2 + cchunk[i] * 16);
+        }
+        auto issue_copy = [&](const uint16_t* src, int64_t stride, const uint32_t* off, int t, int buf)
+                              __attribute__((always_inline)) {
+            const uint16_t* base = src + static_cast<int64_t>(t) * kNk * stride;
+            const uint32_t dst = lds0 + buf * TILE_BYTES;
+            const int last = kv_len - 1 - t * kNk;  // last valid row of this tile
+            if (last >= kNk - 1) {
 #pragma unroll
-    for (int dblk = 0; dblk < D / 32; ++dblk) {
-        const int c = 4 * dblk + 2 * dsub + ((j & 3) >> 1);
-        voff_lo[dblk] = (vrow * CPR + (c ^ sv_lo)) * 16 + (j & 1) * 8;
-        voff_hi[dblk] = ((vrow + 8) * CPR + (c ^ sv_hi)) * 16 + (j & 1) * 8;
-    }
-
-    const float c2 = a.scale * kLog2e;  // exp(s*scale) = exp2(s*c2)
-    f32x16 oacc[D / 32];
+                for (int i = 0; i < PER_WAVE; ++i) lds_dma16(base, off[i], dst + (wave * PER_WAVE + i) * 1024);
+            } else {  // ragged end of the block: rows past it re-read its last row (masked later)
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_ref = -INFINITY;   // exponent reference (log2 units of the scaled score)
-    float m_true = -INFINITY;  // running row maximum
-    float l_run = 0.f;         // this lane's share of the running sum
-    f32x16 sacc[kSub];         // S^T of the current tile, then its probabilities
-    bf16x8 preg[2 * kSub];     // P^T operand of the tile awaiting its PV product
+                for (int i = 0; i < PER_WAVE; ++i) {
+                    const uint32_t o = static_cast<uint32_t>(min(crow[i], last) * stride * 2 + cchunk[i] * 16);
+                    lds_dma16(base, o, dst + (wave * PER_WAVE + i) * 1024);
+                }
+            }
+        };
+        auto issue_k = [&](int t) __attribute__((always_inline)) { issue_copy(kp, ks2, kcp, t, t & 1); };
+        auto issue_v = [&](int t) __attribute__((always_inline)) { issue_copy(vp, vs2, vcp, t, 2 + (t & 1)); };
+        // Ping-pong copies: group 0 copies K tiles, group 1 V tiles, each group's
+        // four waves one instruction at a time from inside their MFMA stream.
+        // Instruction i of wave slot w (w = wave mod WAVES/2) fills chunk
+        // positions [64 (w PER_G + i), +64) of the tile: rows crow0 + RPI i.
+        constexpr int PER_G = INSTR / (WAVES / 2);  // copy instructions per wave per tile
+        constexpr int RPI = 64 / CPR;               // tile rows per copy instruction
+        static_assert(INSTR % (WAVES / 2) == 0, "tile copy must split evenly over a wave group");
+        const int wslot = wave % (WAVES / 2);
+        const int crow0 = wslot * PER_G * RPI + lane / CPR;
+        uint32_t cc16[PER_G];
+#pragma unroll
+        for (int i = 0; i < PER_G; ++i) cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
 
-    auto visible = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < n_tiles && t * kNk < wave_key_end; };
+        // per-lane LDS byte offsets of the operand reads
+        const lds_char* lds = RA_LDS_PTR(char, smem);
+        const int sq = swz<D>(qi);  // K rows sub*32 + qi share swz(qi)
+        uint32_t koff[D / 16];
+#pragma unroll
+        for (int kb = 0; kb < D / 16; ++kb) koff[kb] = (qi * CPR + ((2 * kb + half) ^ sq)) * 16;
+        const int j = lane & 15;                        // lane within its 16-lane group
+        const int dsub = (lane >> 4) & 1;               // which 16 columns of a 32-column block
+        const int vrow = 4 * half + (j >> 2);           // row within a 16-row k-block (first run)
+        const int sv_lo = swz<D>(vrow), sv_hi = swz<D>(vrow + 8);
+        uint32_t voff_lo[D / 32], voff_hi[D / 32];
+#pragma unroll
+        for (int dblk = 0; dblk < D / 32; ++dblk) {
+            const int c = 4 * dblk + 2 * dsub + ((j & 3) >> 1);
+            voff_lo[dblk] = (vrow * CPR + (c ^ sv_lo)) * 16 + (j & 1) * 8;
+            voff_hi[dblk] = ((vrow + 8) * CPR + (c ^ sv_hi)) * 16 + (j & 1) * 8;
+        }
 
-    // mask, row max, reference move, exponentials, row sum, bf16 P^T.
-    auto softmax = [&](int t) __attribute__((always_inline)) {
-        const int kbase = t * kNk;
-        // mask (diagonal / ragged tiles only) and row max, on the raw scores:
-        // the scale is positive, so it is applied once, to the maximum.
-        if (kbase + kNk > wave_full_end) {
+        const float c2 = a.scale * kLog2e;  // exp(s*scale) = exp2(s*c2)
+        f32x16 oacc[D / 32];
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
+        float m_ref = -INFINITY;   // exponent reference (log2 units of the scaled score)
+        float m_true = -INFINITY;  // running row maximum
+        float l_run = 0.f;         // this lane's share of the running sum
+        f32x16 sacc[kSub];         // S^T of the current tile, then its probabilities
+        bf16x8 preg[2 * kSub];     // P^T operand of the tile awaiting its PV product
+
+        auto visible = [&](int t) __attribute__((always_inline)) {
+            return t >= 0 && t < n_tiles && t * kNk < wave_key_end;
+        };
+
+        // mask, row max, reference move, exponentials, row sum, bf16 P^T.
+        auto softmax = [&](int t) __attribute__((always_inline)) {
+            const int kbase = t * kNk;
+            // mask (diagonal / ragged tiles only) and row max, on the raw scores:
+            // the scale is positive, so it is applied once, to the maximum.
+            if (kbase + kNk > wave_full_end) {
+#pragma unroll
+                for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
+                        const bool vis = key < kv_len && (!a.causal || key <= row + mask_offset);
+                        sacc[sub][v] = vis ? sacc[sub][v] : -INFINITY;
+                    }
+                }
+            }
+            // row max: this lane's 16 kSub scores, then the other half-wave's
+            float mt[16 * kSub];
+#pragma unroll
+            for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mt[16 * sub + v] = sacc[sub][v];
+            const float mx = xhalf_max(max_tree<16 * kSub>(mt)) * c2;
+            m_true = vmax(m_true, mx);
+            const bool move = mx > m_ref + kTau;
+            if (__builtin_amdgcn_ballot_w64(move)) {  // rare: re-reference the running state
+                const float m_new = move ? mx : m_ref;
+                const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+                m_ref = m_new;
+            }
+            const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
+            float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
 #pragma unroll
             for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int key = kbase + sub * 32 + 8 * (v / 4) + 4 * half + (v % 4);
-                    const bool vis = key < kv_len && (!a.causal || key <= row + mask_offset);
-                    sacc[sub][v] = vis ? sacc[sub][v] : -INFINITY;
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][v], c2, neg_m));
+                    sacc[sub][v] = p;
+                    ls[v & 3] += p;
                 }
             }
-        }
-        // row max: this lane's 16 kSub scores, then the other half-wave's
-        float mt[16 * kSub];
+            l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mt[16 * sub + v] = sacc[sub][v];
-        const float mx = xhalf_max(max_tree<16 * kSub>(mt)) * c2;
-        m_true = vmax(m_true, mx);
-        const bool move = mx > m_ref + kTau;
-        if (__builtin_amdgcn_ballot_w64(move)) {  // rare: re-reference the running state
-            const float m_new = move ? mx : m_ref;
-            const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;  // 0 when m_ref = -inf
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-            m_ref = m_new;
-        }
-        const float neg_m = (m_ref == -INFINITY) ? 0.f : -m_ref;
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};  // independent partial sums
-#pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][v], c2, neg_m));
-                sacc[sub][v] = p;
-                ls[v & 3] += p;
+            for (int sub = 0; sub < kSub; ++sub) {
+                preg[2 * sub] = pack_bf16x8(sacc[sub], 0);
+                preg[2 * sub + 1] = pack_bf16x8(sacc[sub], 8);
             }
-        }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-#pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
-            preg[2 * sub] = pack_bf16x8(sacc[sub], 0);
-            preg[2 * sub + 1] = pack_bf16x8(sacc[sub], 8);
-        }
-    };
+        };
 
-    // One MFMA half as a software-pipelined operand stream: the QK^T MFMAs of
-    // tile tq (kb-major, sub-tile-minor) then the PV MFMAs of tile tp
-    // (O^T += V^T P^T, 4-k-block x dblk order).  Each operand's LDS read is
-    // issued kPf steps before its MFMA, and a scheduling fence after every step
-    // keeps that distance, so LDS latency hides behind the MFMAs in flight.
-    constexpr int kPf = RA_MFMA_PREFETCH;
-    constexpr int NPV = 2 * kSub * (D / 32), NQK = kSub * (D / 16), NT = NPV + NQK;
-    bf16x8 ops[kPf];  // operands in flight (the first ones may be issued before a barrier)
-    auto load_op_at = [&](const lds_char* vst, const lds_char* kst, int i) __attribute__((always_inline)) -> bf16x8 {
-        if (i < NPV) {
-            const int kb2 = i / (D / 32), dblk = i % (D / 32);
-            const int run = (kb2 * 16) * CPR * 16;
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vst + voff_lo[dblk] + run));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vst + voff_hi[dblk] + run));
-            const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            return __builtin_bit_cast(bf16x8, both);
-        }
-        const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
-        return *(const __attribute__((address_space(3))) bf16x8*)(kst + koff[kb] + sub * 32 * CPR * 16);
-    };
-    // the first kPf operands of a full stream for tile tq (QK^T reads of K(tq))
-    auto preload = [&](int tq) __attribute__((always_inline)) {
-        const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
-#pragma unroll
-        for (int n = 0; n < kPf; ++n) ops[n] = load_op_at(nullptr, kst, NPV + n);
-    };
-    auto mfma_stream = [&]<bool PV, bool QK, bool PRE = false>(int tp, int tq, auto&& hook) __attribute__((always_inline)) {
-        constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NT : NPV, N = I1 - I0;
-        const lds_char* vst = lds + (2 + (tp & 1)) * TILE_BYTES;
-        const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
-        auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 { return load_op_at(vst, kst, i); };
-        auto run_mfma = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+        // One MFMA half as a software-pipelined operand stream: the QK^T MFMAs of
+        // tile tq (kb-major, sub-tile-minor) then the PV MFMAs of tile tp
+        // (O^T += V^T P^T, 4-k-block x dblk order).  Each operand's LDS read is
+        // issued kPf steps before its MFMA, and a scheduling fence after every step
+        // keeps that distance, so LDS latency hides behind the MFMAs in flight.
+        constexpr int kPf = RA_MFMA_PREFETCH;
+        constexpr int NPV = 2 * kSub * (D / 32), NQK = kSub * (D / 16), NT = NPV + NQK;
+        bf16x8 ops[kPf];  // operands in flight (the first ones may be issued before a barrier)
+        auto load_op_at = [&](const lds_char* vst, const lds_char* kst, int i)
+                              __attribute__((always_inline)) -> bf16x8 {
             if (i < NPV) {
                 const int kb2 = i / (D / 32), dblk = i % (D / 32);
-                oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, preg[kb2], oacc[dblk], 0, 0, 0);
-            } else {
-                const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
-                sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kb], kb == 0 ? f32x16{} : sacc[sub], 0,
-                                                                     0, 0);
+                const int run = (kb2 * 16) * CPR * 16;
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vst + voff_lo[dblk] + run));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(vst + voff_hi[dblk] + run));
+                const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                return __builtin_bit_cast(bf16x8, both);
+            }
+            const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
+            return *(const __attribute__((address_space(3))) bf16x8*)(kst + koff[kb] + sub * 32 * CPR * 16);
+        };
+        // the first kPf operands of a full stream for tile tq (QK^T reads of K(tq))
+        auto preload = [&](int tq) __attribute__((always_inline)) {
+            const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
+#pragma unroll
+            for (int n = 0; n < kPf; ++n) ops[n] = load_op_at(nullptr, kst, NPV + n);
+        };
+        auto mfma_stream = [&]<bool PV, bool QK, bool PRE = false>(int tp, int tq, auto&& hook)
+                               __attribute__((always_inline)) {
+            constexpr int I0 = PV ? 0 : NPV, I1 = QK ? NT : NPV, N = I1 - I0;
+            const lds_char* vst = lds + (2 + (tp & 1)) * TILE_BYTES;
+            const lds_char* kst = lds + (tq & 1) * TILE_BYTES;
+            auto load_op = [&](int i) __attribute__((always_inline)) -> bf16x8 { return load_op_at(vst, kst, i); };
+            auto run_mfma = [&](int i, const bf16x8& op) __attribute__((always_inline)) {
+                if (i < NPV) {
+                    const int kb2 = i / (D / 32), dblk = i % (D / 32);
+                    oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, preg[kb2], oacc[dblk], 0, 0, 0);
+                } else {
+                    const int jq = i - NPV, kb = jq / kSub, sub = jq % kSub;
+                    sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, qreg[kb], kb == 0 ? f32x16{} : sacc[sub], 0,
+                                                                         0, 0);
+                }
+            };
+            // step n -> operand index: QK^T first, then PV, so that the scores the
+            // wave's next softmax half reads are complete when the stream ends
+            // (only PV results, not needed until the next MFMA half, drain then)
+            auto idx = [&](int n) __attribute__((always_inline)) {
+                if constexpr (PV && QK) return n < NQK ? NPV + n : n - NQK;
+                else return I0 + n;
+            };
+            if constexpr (!PRE) {
+#pragma unroll
+                for (int n = 0; n < kPf && n < N; ++n) ops[n] = load_op(idx(n));
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) {
+                const bf16x8 op = ops[n % kPf];
+                if (n + kPf < N) ops[n % kPf] = load_op(idx(n + kPf));
+                run_mfma(idx(n), op);
+                hook(n);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // step n -> operand index: QK^T first, then PV, so that the scores the
-        // wave's next softmax half reads are complete when the stream ends
-        // (only PV results, not needed until the next MFMA half, drain then)
-        auto idx = [&](int n) __attribute__((always_inline)) {
-            if constexpr (PV && QK) return n < NQK ? NPV + n : n - NQK;
-            else return I0 + n;
-        };
-        if constexpr (!PRE) {
-#pragma unroll
-            for (int n = 0; n < kPf && n < N; ++n) ops[n] = load_op(idx(n));
-        }
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const bf16x8 op = ops[n % kPf];
-            if (n + kPf < N) ops[n % kPf] = load_op(idx(n + kPf));
-            run_mfma(idx(n), op);
-            hook(n);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    auto no_hook = [](int) __attribute__((always_inline)) {};
+        auto no_hook = [](int) __attribute__((always_inline)) {};
 
 #if RA_MFMA_PINGPONG
-    // Two groups of WAVES/2 waves (one wave per SIMD each), half a tile apart.
-    // Between consecutive barriers one group runs MFMAs (QK^T of tile t, then
-    // PV of tile t-1) while the other runs the softmax of its current tile, so
-    // each SIMD's matrix core and vector ALU work at the same time.  K(t+1)
-    // and V(t) are copied during iteration t and published by its final
-    // barrier; a buffer is refilled only after the barrier that ends its last
-    // reader's phase.
-    static_assert(WAVES % 8 == 0, "ping-pong needs two groups of one wave per SIMD");
-    const int group = wave / (WAVES / 2);
-    // The MFMA half runs the full stream even for a tile this wave cannot see:
-    // P is then zero (valu_half) and the V tile holds finite block values, so
-    // the PV product adds exactly zero, and scores of an unseen tile are never
-    // read.  A group's phase lasts as long as its slowest wave, so skipping
-    // would not shorten it.  Only the first MFMA half (no PV product yet) and
-    // the one after the last tile (no QK^T, no copies) are shortened.
-    // Copies.  Group 0's MFMA half of tile t (global phase 2t) copies K(t+1);
-    // group 1's (phase 2t+1) copies V(t).  Both buffers' last readers
-    // finished in phase 2t-1, each group awaits its copies at the end of its
-    // own MFMA half (K(t+1) is published at the end of phase 2t, V(t) at the
-    // end of phase 2t+1), and neither tile is read before phase 2t+2 -- except
-    // the first operands of the next MFMA stream, which each wave reads from
-    // K(t+1) at the end of its softmax half of tile t (phases 2t+1 and 2t+2),
-    // before the barrier, so that their LDS latency is not exposed at the
-    // start of the stream.  Each wave issues its
-    // PER_G instructions one every kStep MFMA steps over the first half of its
-    // stream, so no wave stalls on a full memory-request queue.  Everything
-    // group-dependent is wave-uniform and selected, not branched on, so both
-    // groups run one MFMA stream.  A tile index past the block copies the last
-    // tile instead (into a buffer no one reads any more; awaited like the
-    // others), and rows past the block re-read its last row.
-    constexpr int kStep = (NT / 2) / PER_G;
-    static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
-    auto mfma_half = [&]<bool PV, bool QK, bool PRE = false>(int t) __attribute__((always_inline)) {
-        const bool gk = group == 0;
-        const int tt = gk ? t + 1 : t;
-        const int tc = min(tt, n_tiles - 1);
-        const int64_t stride = gk ? ks2 : vs2;
-        const uint16_t* src = (gk ? kp : vp) + static_cast<int64_t>(tc) * kNk * stride;
-        const uint32_t stride2 = static_cast<uint32_t>(stride * 2);
-        const int last = kv_len - 1 - tc * kNk;  // last row of the block within tile tc
-        const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
-        if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-        mfma_stream.template operator()<PV, QK, PRE>(t - 1, t, [&](int n) __attribute__((always_inline)) {
-            if (QK && n % kStep == 0 && n / kStep < PER_G) {
-                const int i = n / kStep;
-                const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
-                lds_dma16(src, o, dst + i * 1024);
-            }
-        });
-        if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    };
-    auto valu_half = [&](int t) __attribute__((always_inline)) {
-        if (visible(t)) {
-            softmax(t);
-        } else {
+        // Two groups of WAVES/2 waves (one wave per SIMD each), half a tile apart.
+        // Between consecutive barriers one group runs MFMAs (QK^T of tile t, then
+        // PV of tile t-1) while the other runs the softmax of its current tile, so
+        // each SIMD's matrix core and vector ALU work at the same time.  K(t+1)
+        // and V(t) are copied during iteration t and published by its final
+        // barrier; a buffer is refilled only after the barrier that ends its last
+        // reader's phase.
+        static_assert(WAVES % 8 == 0, "ping-pong needs two groups of one wave per SIMD");
+        const int group = wave / (WAVES / 2);
+        // The MFMA half runs the full stream even for a tile this wave cannot see:
+        // P is then zero (valu_half) and the V tile holds finite block values, so
+        // the PV product adds exactly zero, and scores of an unseen tile are never
+        // read.  A group's phase lasts as long as its slowest wave, so skipping
+        // would not shorten it.  Only the first MFMA half (no PV product yet) and
+        // the one after the last tile (no QK^T, no copies) are shortened.
+        // Copies.  Group 0's MFMA half of tile t (global phase 2t) copies K(t+1);
+        // group 1's (phase 2t+1) copies V(t).  Both buffers' last readers
+        // finished in phase 2t-1, each group awaits its copies at the end of its
+        // own MFMA half (K(t+1) is published at the end of phase 2t, V(t) at the
+        // end of phase 2t+1), and neither tile is read before phase 2t+2 -- except
+        // the first operands of the next MFMA stream, which each wave reads from
+        // K(t+1) at the end of its softmax half of tile t (phases 2t+1 and 2t+2),
+        // before the barrier, so that their LDS latency is not exposed at the
+        // start of the stream.  Each wave issues its
+        // PER_G instructions one every kStep MFMA steps over the first half of its
+        // stream, so no wave stalls on a full memory-request queue.  Everything
+        // group-dependent is wave-uniform and selected, not branched on, so both
+        // groups run one MFMA stream.  A tile index past the block copies the last
+        // tile instead (into a buffer no one reads any more; awaited like the
+        // others), and rows past the block re-read its last row.
+        constexpr int kStep = (NT / 2) / PER_G;
+        static_assert(kStep >= 1 && (NT / 2) % PER_G == 0, "copies must split the first half of the stream evenly");
+        auto mfma_half = [&]<bool PV, bool QK, bool PRE = false>(int t) __attribute__((always_inline)) {
+            const bool gk = group == 0;
+            const int tt = gk ? t + 1 : t;
+            const int tc = min(tt, n_tiles - 1);
+            const int64_t stride = gk ? ks2 : vs2;
+            const uint16_t* src = (gk ? kp : vp) + static_cast<int64_t>(tc) * kNk * stride;
+            const uint32_t stride2 = static_cast<uint32_t>(stride * 2);
+            const int last = kv_len - 1 - tc * kNk;  // last row of the block within tile tc
+            const uint32_t dst = lds0 + (gk ? (tt & 1) : 2 + (tt & 1)) * TILE_BYTES + wslot * PER_G * 1024;
+            if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
+            mfma_stream.template operator()<PV, QK, PRE>(t - 1, t, [&](int n) __attribute__((always_inline)) {
+                if (QK && n % kStep == 0 && n / kStep < PER_G) {
+                    const int i = n / kStep;
+                    const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
+                    lds_dma16(src, o, dst + i * 1024);
+                }
+            });
+            if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        };
+        auto valu_half = [&](int t) __attribute__((always_inline)) {
+            if (visible(t)) {
+                softmax(t);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 2 * kSub; ++i) preg[i] = bf16x8{};
-        }
-    };
-    // Both groups run the same loop body -- MFMA half of tile t, barrier,
-    // softmax half of tile t, barrier -- but group 1 first passes one extra
-    // barrier (and group 0 one after its final PV half), so group 1 runs one
-    // phase behind and both groups pass the same number of barriers.
-    // Global phase 2t carries group 0's MFMA half of tile t and group 1's
-    // softmax half of tile t-1; phase 2t+1 the other way round.
-    // barrier with no wait for outstanding LDS reads (the first operands of
-    // the next MFMA stream, read from a tile published one phase earlier); the
-    // memory clobber keeps the compiler from moving accesses across it
-    auto barrier = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
-    if (n_tiles > 0) {
-        issue_k(0);
-        wait_vmem_all();
-        __syncthreads();
-        if (group == 1) barrier();
-        // first tile: no PV product yet
-        mfma_half.template operator()<false, true>(0);
-        wait_vmem_all();
-        barrier();
-        valu_half(0);
-        if (1 < n_tiles) preload(1);
-        barrier();
-        for (int t = 1; t < n_tiles; ++t) {
-            mfma_half.template operator()<true, true, true>(t);
+                for (int i = 0; i < 2 * kSub; ++i) preg[i] = bf16x8{};
+            }
+        };
+        // Both groups run the same loop body -- MFMA half of tile t, barrier,
+        // softmax half of tile t, barrier -- but group 1 first passes one extra
+        // barrier (and group 0 one after its final PV half), so group 1 runs one
+        // phase behind and both groups pass the same number of barriers.
+        // Global phase 2t carries group 0's MFMA half of tile t and group 1's
+        // softmax half of tile t-1; phase 2t+1 the other way round.
+        // barrier with no wait for outstanding LDS reads (the first operands of
+        // the next MFMA stream, read from a tile published one phase earlier); the
+        // memory clobber keeps the compiler from moving accesses across it
+        auto barrier = []() __attribute__((always_inline)) { asm volatile("s_barrier" ::: "memory"); };
+        if (n_tiles > 0) {
+            issue_k(0);
+            wait_vmem_all();
+            __syncthreads();
+            if (group == 1) barrier();
+            // first tile: no PV product yet
+            mfma_half.template operator()<false, true>(0);
             wait_vmem_all();
             barrier();
-            valu_half(t);
-            if (t + 1 < n_tiles) preload(t + 1);
+            valu_half(0);
+            if (1 < n_tiles) preload(1);
             barrier();
+            for (int t = 1; t < n_tiles; ++t) {
+                mfma_half.template operator()<true, true, true>(t);
+                wait_vmem_all();
+                barrier();
+                valu_half(t);
+                if (t + 1 < n_tiles) preload(t + 1);
+                barrier();
+            }
+            // PV product of the last tile (no copies).  Group 0 then passes the
+            // barrier that ends group 1's last softmax half; group 1 runs its
+            // final PV half with no barrier after it, while group 0 writes out.
+            mfma_half.template operator()<true, false>(n_tiles);
+            if (group == 0) barrier();
         }
-        // PV product of the last tile (no copies).  Group 0 then passes the
-        // barrier that ends group 1's last softmax half; group 1 runs its
-        // final PV half with no barrier after it, while group 0 writes out.
-        mfma_half.template operator()<true, false>(n_tiles);
-        if (group == 0) barrier();
-    }
 #else
-    if (n_tiles > 0) {
-        issue_k(0);
-        issue_v(0);
-    }
-    for (int t = 0; t < n_tiles; ++t) {
-        wait_vmem_all();
-        __syncthreads();
-        if (t + 1 < n_tiles) {
-            issue_k(t + 1);
-            issue_v(t + 1);
+        if (n_tiles > 0) {
+            issue_k(0);
+            issue_v(0);
         }
-        if (!visible(t)) continue;  // nothing visible to this wave here
-        mfma_stream.template operator()<false, true>(t, t, no_hook);
-        softmax(t);
-        mfma_stream.template operator()<true, false>(t, t, no_hook);
-    }
+        for (int t = 0; t < n_tiles; ++t) {
+            wait_vmem_all();
+            __syncthreads();
+            if (t + 1 < n_tiles) {
+                issue_k(t + 1);
+                issue_v(t + 1);
+            }
+            if (!visible(t)) continue;  // nothing visible to this wave here
+            mfma_stream.template operator()<false, true>(t, t, no_hook);
+            softmax(t);
+            mfma_stream.template operator()<true, false>(t, t, no_hook);
+        }
 #endif
 
-    // Epilogue.  The partial (oacc, l_run) is referenced to exp2(m_ref); its
-    // row maximum is m_true.  Written as is (re-referenced to m_true), or --
-    // with a.accumulate -- merged into the running state (o, m, l) of the row
-    // with the same online-softmax rule as ra_lse_merge:
-    //   m = max(m_a, m_p);  w_x = exp(m_x - m) (0 if m_x = -inf).
-    const float l_ref = xhalf_sum(l_run);
-    if (row < a.q_len) {
-        const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + row;
-        float* const mrow = a.m + split * a.part_ml_stride;
-        float* const lrow = a.l + split * a.part_ml_stride;
-        float* orow = a.o + split * a.part_o_stride + idx * D;
-        float m_out = m_true;  // log2 units
-        float wa = 0.f, l_a = 0.f;
-        float wp = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
-        f32x4* const dst = reinterpret_cast<f32x4*>(orow + 4 * half);  // + (8 dblk + 2 g) vectors
-        if (a.accumulate) {
-            // every load of the running state is issued before the first store,
-            // so the row's read-modify-write costs one memory round trip
-            const float m_a = mrow[idx] * kLog2e;  // -inf stays -inf
-            l_a = lrow[idx];
-            f32x4 prev[D / 32][4];
+        // Epilogue.  The partial (oacc, l_run) is referenced to exp2(m_ref); its
+        // row maximum is m_true.  Written as is (re-referenced to m_true), or --
+        // with a.accumulate -- merged into the running state (o, m, l) of the row
+        // with the same online-softmax rule as ra_lse_merge:
+        //   m = max(m_a, m_p);  w_x = exp(m_x - m) (0 if m_x = -inf).
+        const float l_ref = xhalf_sum(l_run);
+        if (row < a.q_len) {
+            const int64_t idx = (static_cast<int64_t>(b) * a.Hq + h) * a.q_len + row;
+            float* const mrow = a.m + split * a.part_ml_stride;
+            float* const lrow = a.l + split * a.part_ml_stride;
+            float* orow = a.o + split * a.part_o_stride + idx * D;
+            float m_out = m_true;  // log2 units
+            float wa = 0.f, l_a = 0.f;
+            float wp = (m_true == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_true);
+            f32x4* const dst = reinterpret_cast<f32x4*>(orow + 4 * half);  // + (8 dblk + 2 g) vectors
+            if (a.accumulate) {
+                // every load of the running state is issued before the first store,
+                // so the row's read-modify-write costs one memory round trip
+                const float m_a = mrow[idx] * kLog2e;  // -inf stays -inf
+                l_a = lrow[idx];
+                f32x4 prev[D / 32][4];
 #pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk)
+                for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) prev[dblk][g] = dst[8 * dblk + 2 * g];
-            m_out = fmaxf(m_a, m_true);
-            wa = (m_a == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_a - m_out);
-            wp = (m_true == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_out);
+                    for (int g = 0; g < 4; ++g) prev[dblk][g] = dst[8 * dblk + 2 * g];
+                m_out = fmaxf(m_a, m_true);
+                wa = (m_a == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_a - m_out);
+                wp = (m_true == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_out);
 #pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk)
+                for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 pv = prev[dblk][g];
-                    dst[8 * dblk + 2 * g] = f32x4{__builtin_fmaf(wa, pv[0], oacc[dblk][4 * g] * wp),
-                                                  __builtin_fmaf(wa, pv[1], oacc[dblk][4 * g + 1] * wp),
-                                                  __builtin_fmaf(wa, pv[2], oacc[dblk][4 * g + 2] * wp),
-                                                  __builtin_fmaf(wa, pv[3], oacc[dblk][4 * g + 3] * wp)};
-                }
-        } else {
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 pv = prev[dblk][g];
+                        dst[8 * dblk + 2 * g] = f32x4{__builtin_fmaf(wa, pv[0], oacc[dblk][4 * g] * wp),
+                                                      __builtin_fmaf(wa, pv[1], oacc[dblk][4 * g + 1] * wp),
+                                                      __builtin_fmaf(wa, pv[2], oacc[dblk][4 * g + 2] * wp),
+                                                      __builtin_fmaf(wa, pv[3], oacc[dblk][4 * g + 3] * wp)};
+                    }
+            } else {
 #pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk)
+                for (int dblk = 0; dblk < D / 32; ++dblk)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    dst[8 * dblk + 2 * g] = f32x4{oacc[dblk][4 * g] * wp, oacc[dblk][4 * g + 1] * wp,
-                                                  oacc[dblk][4 * g + 2] * wp, oacc[dblk][4 * g + 3] * wp};
+                    for (int g = 0; g < 4; ++g)
+                        dst[8 * dblk + 2 * g] = f32x4{oacc[dblk][4 * g] * wp, oacc[dblk][4 * g + 1] * wp,
+                                                      oacc[dblk][4 * g + 2] * wp, oacc[dblk][4 * g + 3] * wp};
+            }
+            if (half == 0) {
+                mrow[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
+                lrow[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
+            }
         }
-        if (half == 0) {
-            mrow[idx] = (m_out == -INFINITY) ? -INFINITY : m_out * kLn2;
-            lrow[idx] = __builtin_fmaf(wa, l_a, wp * l_ref);
-        }
-    }
-    if (!a.queue) break;
+        if (!a.queue) break;
     }  // tile loop
     if (a.queue && tid == 0) finish_claims(a.queue, gridDim.x);
 }
