@@ -33,7 +33,9 @@
 // dq_kernel runs eight waves in the forward kernel's ping-pong (two groups
 // of one wave per SIMD, half a tile apart); dkdv_kernel runs eight waves
 // (256 keys) that share each query tile, two per SIMD, whose MFMAs and
-// vector work interleave as they fall.
+// vector work interleave as they fall; a wave raises its priority while it
+// issues its S and dP chains, so that those win the SIMD's issue over the
+// other wave's vector work.
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -445,8 +447,6 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
     }
     const int n_tiles = (a.q_len - row_start + kTile - 1) / kTile;
 
-    TileReads<D> rd;
-    rd.init(lane);
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(RA_LDS_PTR(char, smem)));
     const lds_char* lds = RA_LDS_PTR(char, smem);
 
@@ -506,6 +506,14 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         }
         const int rb = row_start + (st % n_tiles) * kTile;
         if (rb + kTile <= wave_row_start) continue;  // no row of this tile sees this wave's keys
+        // operand-read offsets from a lane index recomputed per tile (volatile:
+        // not hoisted, so they are not kept live across the copies and barrier)
+        TileReads<D> rd;
+        {
+            int ln;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+            rd.init(ln);
+        }
         const lds_char* qt = lds + (st & 1) * BUF;
         const lds_char* gt = qt + TB;
         const float* ls = reinterpret_cast<const float*>(smem + (st & 1) * BUF + 2 * TB);
@@ -516,8 +524,10 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
             // S = Q K^T, then P; P^T (bf16) feeds dV at once so that the fp32
             // scores die before dP is formed
             f32x16 s = f32x16{};
+            __builtin_amdgcn_s_setprio(1);  // the MFMA chain first on this SIMD
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
+            __builtin_amdgcn_s_setprio(0);
             // P; register v holds row rb + 4 half + i of the tile, with the
             // compile-time i = 32 qb + 8 (v/4) + v%4.  Mask (edge tiles only):
             // masked scores become -inf, so that their exp2 is exactly 0; a
@@ -551,8 +561,10 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
             }
             // dP = dO V^T;  dS = P (dP - delta), with P taken back from its bf16 copy
             f32x16 dp = f32x16{};
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kb = 0; kb < D / 16; ++kb) dp = MFMA(rd.rows(gt, qb, kb), vreg[kb], dp);
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int rt = 32 * qb + 8 * g + 4 * half;
