@@ -99,24 +99,59 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
 
 
-def sample_rows(seq_len, n_pos, n_samples, heads, seed=1, first_last_every=None):
-    """Seeded, stratified choice of (head, token) query rows to check.
+def sample_rows(seq_len, n_pos, n_samples, heads, seed=1, first_last_every=None, share=None,
+                layout="contiguous"):
+    """Seeded, stratified choice of exactly ``n_samples`` distinct (head, token)
+    query rows to check.
 
-    Always includes token 0 and the first and last token of every block of
-    ``first_last_every`` tokens (default seq_len // n_pos), each on a seeded
-    head; the rest are drawn uniformly.  Returns (heads, tokens) int64 arrays
-    sorted by (head, token), without duplicates.
+    Rows are drawn from every token of the sequence, or with ``share = i`` only
+    from ring position i's tokens under ``layout`` (contiguous: tokens
+    [i Sb, (i + 1) Sb); striped: tokens i + r N), Sb = seq_len // n_pos.
+    Always includes the first and last token of every block of
+    ``first_last_every`` tokens (default Sb) that the choice may hold -- for a
+    share its first and last token -- and token 0 when it may, each on a seeded
+    head; the rest are drawn uniformly (seeded) until exactly n_samples
+    distinct pairs are held.  Returns (heads, tokens) int64 arrays sorted by
+    (head, token).
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    blk = first_last_every or max(1, seq_len // max(1, n_pos))
-    forced = sorted({0, seq_len - 1} | {b for b in range(0, seq_len, blk)}
-                    | {min(seq_len - 1, b + blk - 1) for b in range(0, seq_len, blk)})
-    hs = list(rng.integers(0, heads, size=len(forced)))
-    ts = list(forced)
-    need = max(0, n_samples - len(ts))
-    hs += list(rng.integers(0, heads, size=need))
-    ts += list(rng.integers(0, seq_len, size=need))
-    pairs = sorted(set(zip((int(h) for h in hs), (int(t) for t in ts))))
-    h = np.array([p[0] for p in pairs], dtype=np.int64)
-    t = np.array([p[1] for p in pairs], dtype=np.int64)
+    sb = max(1, seq_len // max(1, n_pos))
+    if share is None:
+        n_tok = seq_len
+
+        def token(r):
+            return r
+        blk = first_last_every or sb
+        forced_rows = {0, seq_len - 1} | set(range(0, seq_len, blk)) | \
+            {min(seq_len - 1, b + blk - 1) for b in range(0, seq_len, blk)}
+    else:
+        if not 0 <= share < n_pos or seq_len % n_pos:
+            raise ValueError("share must name a ring position of an evenly split sequence")
+        n_tok = sb
+
+        def token(r):
+            return share + r * n_pos if layout == "striped" else share * sb + r
+        forced_rows = {0, sb - 1}
+    if n_samples > heads * n_tok:
+        raise ValueError(f"{n_samples} distinct rows requested, only {heads * n_tok} exist")
+    chosen = []
+    seen = set()
+
+    def add(h, t):
+        if len(chosen) < n_samples and (h, t) not in seen:
+            seen.add((h, t))
+            chosen.append((h, t))
+
+    forced = sorted(forced_rows)
+    for r, h in zip(forced, rng.integers(0, heads, size=len(forced))):
+        add(int(h), int(token(r)))
+    while len(chosen) < n_samples:
+        need = n_samples - len(chosen)
+        hs = rng.integers(0, heads, size=need)
+        rs = rng.integers(0, n_tok, size=need)
+        for h, r in zip(hs, rs):
+            add(int(h), int(token(int(r))))
+    chosen.sort()
+    h = np.array([c[0] for c in chosen], dtype=np.int64)
+    t = np.array([c[1] for c in chosen], dtype=np.int64)
     return h, t

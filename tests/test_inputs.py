@@ -1,6 +1,7 @@
 """The seeded input generator (CPU only): Philox4x32-10 known answers,
 bfloat16 rounding, shard consistency and the N(0,1) distribution."""
 import numpy as np
+import pytest
 import torch
 
 import ra_inputs
@@ -56,8 +57,28 @@ def test_standard_normal_moments():
 def test_sample_rows_are_stratified_and_unique():
     h, t = ra_inputs.sample_rows(4096, 4, 300, heads=8, seed=1)
     pairs = set(zip(h.tolist(), t.tolist()))
-    assert len(pairs) == len(h) >= 290
+    assert len(pairs) == len(h) == 300
     ts = set(t.tolist())
     for b in range(0, 4096, 1024):
         assert b in ts and b + 1023 in ts
     assert np.all((h >= 0) & (h < 8))
+
+
+def test_sample_rows_exact_count_and_share():
+    """Exactly the requested number of distinct rows, also where draws collide
+    often (few tokens), and a share's rows lie on its position's tokens."""
+    h, t = ra_inputs.sample_rows(64, 4, 500, heads=8, seed=1)
+    assert len(set(zip(h.tolist(), t.tolist()))) == len(h) == 500
+    with pytest.raises(ValueError):
+        ra_inputs.sample_rows(64, 4, 513, heads=8, seed=1)
+    for lay in ("striped", "contiguous"):
+        h, t = ra_inputs.sample_rows(1 << 20, 32, 4096, heads=32, seed=1, share=31, layout=lay)
+        assert len(set(zip(h.tolist(), t.tolist()))) == len(h) == 4096
+        if lay == "striped":
+            assert np.all(t % 32 == 31) and {31, 31 + 32 * 32767} <= set(t.tolist())
+        else:
+            assert np.all(t // 32768 == 31) and {31 * 32768, 32 * 32768 - 1} <= set(t.tolist())
+    # the draw is seeded
+    a = ra_inputs.sample_rows(4096, 4, 300, heads=8, seed=5)
+    b = ra_inputs.sample_rows(4096, 4, 300, heads=8, seed=5)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
