@@ -214,6 +214,7 @@ def test_config3_causal_contiguous_sampled():
     assert st["blocks_skipped"] == N * (N - 1) // 2
     assert st["flops"] == 4 * D * H * S * (S + 1) // 2
     sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
+    assert len(set(zip(sh.tolist(), stt.tolist()))) == 4096
     gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "contiguous", 0, True, "bf16")
 
 

@@ -36,6 +36,7 @@ def test_config4_causal_striped_full_ring_and_share():
     o, lse, st = gh.run_ring(qs, ks, vs, N, 0, "striped", True, stats=True)
     assert st["blocks_skipped"] == 0 and st["flops"] == 4 * D * H * S * (S + 1) // 2
     sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
+    assert len(set(zip(sh.tolist(), stt.tolist()))) == 4096
     gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "striped", 0, True, "bf16")
     # one position's share (the benchmarked unit) equals that position of the full ring, bitwise
     gh.say("ra_ring_forward config4 share")
@@ -60,16 +61,26 @@ def test_config5_gqa_striped_share_sampled():
     o, lse, st = gh.run_ring(qs, ks, vs, N, i, "striped", True, stats=True)
     assert st["block_launches"] == N and st["merge_launches"] == 1  # merges fused; one finalising pass
     assert abs(st["flops"] - 2.8148e14) / 2.8148e14 < 1e-4
-    sb = S // N
-    rng = np.random.Generator(np.random.PCG64(1))
-    rows = np.unique(np.concatenate([[0, sb - 1], rng.integers(0, sb, 4094)]))
-    heads = rng.integers(0, Hq, rows.size)
-    sel_t = i + N * rows
+    heads, sel_t = ra_inputs.sample_rows(S, N, 4096, heads=Hq, seed=1, share=i, layout="striped")
+    assert len(set(zip(heads.tolist(), sel_t.tolist()))) == 4096
 
     def qrows(h, t):
         return q_share[0][h, (t - i) // N]
 
     gh.compare_rows(o, lse, qrows, kn, vn, heads, sel_t, N, "striped", i, True, "bf16")
+    # Rows of the softmax sum to one: with V = 1 every output element is exactly
+    # sum(p) / sum(p) = 1 before rounding, so on every row of the share the bf16
+    # output lies within one bf16 spacing of 1 (the numerator sums the
+    # bf16-rounded probabilities, the denominator the fp32 ones) and almost all
+    # elements are exactly 1; lse does not depend on V.
+    gh.say("ra_ring_forward config5 share, V = 1")
+    del vs
+    ones = torch.ones_like(ks)
+    o1, lse1, _ = gh.run_ring(qs, ks, ones, N, i, "striped", True)
+    dev = (o1.float() - 1.0).abs()
+    assert float(dev.max()) <= 2.0 ** -7, float(dev.max())
+    assert float((dev == 0).float().mean()) >= 0.99
+    assert torch.equal(lse1, lse)
 
 
 @pytest.mark.timeout(600)
@@ -93,6 +104,36 @@ def test_dominant_self_key_at_scale():
     ra.ra_stripe_permute(o2, full2, layout="striped", inverse=True, n_pos=N)
     torch.cuda.synchronize()
     dev = np.max(np.abs(gh.to_host_f64(full2)[0][:, 1:-1] - v_f[:, 2:]), axis=-1)
+    assert np.min(dev) > 0.1  # no row collapsed onto its (masked) future key
+
+
+@pytest.mark.timeout(900)
+def test_dominant_self_key_llama_map_share():
+    """The dominant and shifted self-key constructions over the 1M-token striped
+    map of 32 positions (MHA, 2 heads), on every row of position 5's share
+    (32768 queries against 32 key/value blocks): with k = 8 q each row's own key
+    dominates, so O_t = v_t; with keys shifted one token (k_c = 8 q_(c-1)) each
+    row's dominant key is its successor, which the causal mask must hide, so no
+    row may collapse onto v_(t+1)."""
+    H, S, D, N, i = 2, 1 << 20, 128, 32, 5
+    sb = S // N
+    gh.say("ra_ring_forward dominant self key, 1M striped over 32")
+    kn = ra_inputs.normal((1, H, S, D), ra_inputs.STREAM_Q, seed=19, dtype="bf16", scale=8.0)
+    vn = ra_inputs.normal((1, H, S, D), ra_inputs.STREAM_V, seed=19, dtype="bf16")
+    q_share = ra_inputs.normal((1, H, S, D), ra_inputs.STREAM_Q, seed=19, dtype="bf16", t0=i, t_stride=N,
+                               n_rows=sb)
+    ks = gh.shards_on_device(kn, N, "striped", "bf16")
+    vs = gh.shards_on_device(vn, N, "striped", "bf16")
+    qs = gh.to_device(q_share, "bf16")[None]
+    o, _, _ = gh.run_ring(qs, ks, vs, N, i, "striped", True)
+    v_rows = ra_inputs.bf16_to_f32(vn[0][:, i::N])          # v_t for the share's tokens t = i + N r
+    assert np.max(np.abs(gh.to_host_f64(o[0, 0]) - v_rows)) <= 2e-2
+    del ks, kn
+    ksh = ra_inputs.normal((1, H, S, D), ra_inputs.STREAM_Q, seed=19, dtype="bf16", t0=-1, scale=8.0)
+    ks2 = gh.shards_on_device(ksh, N, "striped", "bf16")
+    o2, _, _ = gh.run_ring(qs, ks2, vs, N, i, "striped", True)
+    v_next = ra_inputs.bf16_to_f32(vn[0][:, i + 1::N])     # v_(t+1)
+    dev = np.max(np.abs(gh.to_host_f64(o2[0, 0]) - v_next), axis=-1)
     assert np.min(dev) > 0.1  # no row collapsed onto its (masked) future key
 
 
