@@ -17,6 +17,17 @@ import ring_attention_step_amd as ra
 
 TOL = {"f32": {"o": 1e-5, "lse": 1e-5}, "bf16": {"o": 2e-2, "lse": 1e-3}}
 
+# Gradient tolerances (relative factor of grad_close).  "bf16": the MFMA
+# backward rounds P (for dV) and dS (for dQ, dK) to bfloat16, and bfloat16
+# rings feed the forward's bf16-rounded output into delta = dO . O: every
+# term of a gradient sum carries an independent relative error of at most
+# 2^-8 (8 significant bits), so an element's error is about 2^-8/sqrt(3)
+# times the root-sum-square of its terms, which the row's RMS over head_dim
+# estimates; 2^-5 of the row RMS is above the largest such error over 10^8
+# elements (about 6.5 sigma, 0.015 of the row RMS).  "fp32": products and
+# probabilities kept in binary32.
+GRAD_RTOL = {"bf16": 2.0 ** -5, "fp32": 1e-4}
+
 
 def say(*args):
     """Name the GPU step about to run (flushed, so it survives a crash)."""
@@ -102,3 +113,30 @@ def run_ring(q_sh, k_sh, v_sh, n_pos, first_pos, layout, causal, **kw):
     torch.cuda.synchronize()
     assert n_run == o.shape[0]
     return o, lse, stats
+
+
+def grad_close(got, want, rtol, what):
+    """Elementwise gradient check against the oracle:
+        |got - want| <= rtol * (|want| + rms_row(want) + 2^-4 rms(want))
+    rms_row is the RMS of the element's row over head_dim (the last axis), the
+    scale of the rounding errors of the sums that form the row; the last term
+    is a floor for rows whose exact value is (near) zero.  Returns the largest
+    ratio of error to bound."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    if want.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    row_rms = np.sqrt(np.mean(want * want, axis=-1, keepdims=True))
+    floor = 2.0 ** -4 * float(np.sqrt(np.mean(want * want)))
+    bound = rtol * (np.abs(want) + row_rms + floor)
+    err = np.abs(got - want)
+    zero = bound == 0
+    assert not np.any(err[zero] > 0), f"{what}: nonzero error where the reference is exactly zero"
+    ratio = np.where(zero, 0.0, err / np.where(zero, 1.0, bound))
+    worst = float(np.max(ratio))
+    at = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert worst <= 1.0, (f"{what}: |GPU - oracle| = {float(err[at]):.3e} at {tuple(int(i) for i in at)} exceeds "
+                          f"{float(bound[at]):.3e} (ref {float(want[at]):.3e}, row rms {float(row_rms[at[:-1]][0]):.3e})")
+    return worst

@@ -5,10 +5,11 @@ dK, dV given the rows' full-key-set lse and delta; the oracle computes the
 same share (``oracle.grads`` with lse/delta).  Rings: ra_ring_backward's
 gradients against ``oracle.attention_grads`` in global token order.
 
-Tolerance: max |GPU - oracle| <= tol * max(1, max |oracle|) per tensor, with
-tol = 1e-4 for the fp32-arithmetic kernels (binary32 or bfloat16 inputs
-widened exactly) and 2e-2 where bfloat16 MFMA products round P and dS to
-bfloat16.
+Tolerance: elementwise, |GPU - oracle| <= rtol (|oracle| + row RMS + 2^-4 RMS)
+(tests/gpu_helpers.py grad_close), with rtol = 1e-4 for the fp32-arithmetic
+kernels on binary32 inputs and 2^-5 where bfloat16 enters a gradient sum (the
+MFMA kernels round P and dS to bfloat16; bfloat16 rings feed the forward's
+bfloat16 output into delta).
 """
 import numpy as np
 import pytest
@@ -70,7 +71,7 @@ def test_block_bwd_matches_oracle(dtype, D, force_simt):
     g = gh.to_device(np.ascontiguousarray(gn.transpose(0, 2, 1, 3)), dtype).permute(0, 2, 1, 3)
     k, v = gh.to_device(kn, dtype), gh.to_device(vn, dtype)
     mfma = dtype == "bf16" and D in (64, 128) and not force_simt
-    tol = 2e-2 if mfma else 1e-4
+    tol = gh.GRAD_RTOL["bf16"] if mfma else gh.GRAD_RTOL["fp32"]
     grp = Hq // Hkv
     for off in OFFSETS:
         causal = off is not None
@@ -102,7 +103,7 @@ def test_block_bwd_matches_oracle(dtype, D, force_simt):
                              flags=ra.RA_BLOCK_FORCE_SIMT if force_simt else 0)
         torch.cuda.synchronize()
         for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-            _close(gh.to_host_f64(got), want[name], tol, f"{name} off={off}")
+            gh.grad_close(gh.to_host_f64(got), want[name], tol, f"{name} off={off}")
 
 
 def test_block_bwd_accumulates_and_empty_cases():
@@ -161,7 +162,7 @@ def test_block_bwd_rows_without_keys_mfma(D):
     ra.ra_block_attn_bwd(q, k, v, g, lse_d, dlt_d, dq, dk, dv, causal=True, q_pos0=off, k_pos0=0)
     torch.cuda.synchronize()
     for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _close(gh.to_host_f64(got), want[name], 2e-2, name)
+        gh.grad_close(gh.to_host_f64(got), want[name], gh.GRAD_RTOL["bf16"], name)
     # every row -inf on a non-causal block: nothing changes
     for x in (dq, dk, dv):
         x.fill_(0.5)
@@ -194,12 +195,11 @@ def test_ring_backward_matches_oracle(lay, causal, dtype, D, N, S):
         ra.ra_stripe_permute(sh, full, layout=lay, inverse=True, n_pos=N)
     torch.cuda.synchronize()
     want = oracle.attention_grads(qn, kn, vn, gn, causal=causal)
-    mfma = dtype == "bf16" and D in (64, 128)
     # the backward consumes the GPU forward's bf16 output and fp32 lse, so bf16
     # rings carry that rounding too
-    tol = 2e-2 if (mfma or dtype == "bf16") else 1e-4
+    tol = gh.GRAD_RTOL["bf16"] if dtype == "bf16" else gh.GRAD_RTOL["fp32"]
     for name, got, ref in (("dq", dq_g, want[0]), ("dk", dk_g, want[1]), ("dv", dv_g, want[2])):
-        _close(gh.to_host_f64(got), ref, tol, name)
+        gh.grad_close(gh.to_host_f64(got), ref, tol, name)
 
 
 def test_mfma_backward_runs_and_differs_from_vector_path():
@@ -230,7 +230,7 @@ def test_mfma_backward_runs_and_differs_from_vector_path():
     torch.cuda.synchronize()
     for a_, b_ in zip(*outs):
         assert not torch.equal(a_, b_)
-        assert torch.max(torch.abs(a_ - b_)) <= 2e-2 * max(1.0, float(torch.max(torch.abs(b_))))
+        gh.grad_close(gh.to_host_f64(a_), gh.to_host_f64(b_), gh.GRAD_RTOL["bf16"], "mfma vs vector path")
 
 
 def test_ring_backward_gqa_moderate_size_all_gradients():
@@ -252,15 +252,19 @@ def test_ring_backward_gqa_moderate_size_all_gradients():
     torch.cuda.synchronize()
     want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
     for name, got, ref in zip(("dq", "dk", "dv"), outs, want):
-        _close(gh.to_host_f64(got), ref, 2e-2, name)
+        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name)
 
 
 @pytest.mark.timeout(900)
 def test_backward_256k_share_sampled_rows_and_identities():
-    """The causal 256K striped share at full size: dQ on sampled rows against the
-    oracle, and dK / dV through identities that hold at any size: per key/value
-    head, sum_c dK_c = 0, sum_c dV_c = sum_t dO_t (t over the share's rows), and
-    <Q, dQ> over the group's query heads = <K, dK>."""
+    """The causal 256K striped share at full size, elementwise against the oracle:
+    dQ on 1024 distinct sampled rows of the share (all heads); dK and dV on 256
+    sampled keys of two heads drawn from every key/value block, among the keys of
+    the last 4096 tokens of the sequence -- the share's rows that see them are
+    its last 512, whose full-key-set lse and delta the oracle computes (about
+    1.3e8 visible pairs a head).  Plus identities that hold at any size: per
+    key/value head, sum_c dK_c = 0, sum_c dV_c = sum_t dO_t (t over the share's
+    rows), and <Q, dQ> over the group's query heads = <K, dK>."""
     gh.say("ra_ring_backward 256k share")
     B, H, S, D, N, i = 1, 8, 262144, 128, 8, 7
     sb = S // N
@@ -280,10 +284,10 @@ def test_backward_256k_share_sampled_rows_and_identities():
                              causal=True, stats=True)
     torch.cuda.synchronize()
     assert st["block_launches"] == N and st["blocks_skipped"] == 0
-    # sampled dQ rows
-    sh, stt = ra_inputs.sample_rows(S, N, 256, heads=H, seed=1)
-    sel = (stt % N) == i
-    sh, stt = sh[sel], stt[sel]
+    rtol = gh.GRAD_RTOL["bf16"]
+    # dQ: 1024 distinct rows of the share
+    sh, stt = ra_inputs.sample_rows(S, N, 1024, heads=H, seed=1, share=i, layout="striped")
+    assert len(set(zip(sh.tolist(), stt.tolist()))) == 1024
     rr = (stt - i) // N
     got = gh.to_host_f64(dq[0, 0][torch.as_tensor(sh, device="cuda"), torch.as_tensor(rr, device="cuda")])
     want = np.empty_like(got)
@@ -292,7 +296,22 @@ def test_backward_256k_share_sampled_rows_and_identities():
         r = oracle.grads(qn[0, h][rr[idx]], kn[0, h], vn[0, h], gn[0, h][rr[idx]], q_pos=stt[idx], causal=True,
                          key_grads=False)
         want[idx] = r["dq"]
-    _close(got, want, 2e-2, "dq sampled rows")
+    gh.grad_close(got, want, rtol, "dq, 1024 sampled share rows")
+    # dK, dV: sampled keys of the last 4096 tokens, every block j (local rows c >= sb - 512)
+    rows_late = np.arange(sb - 512, sb)
+    t_late = i + N * rows_late
+    rng = np.random.Generator(np.random.PCG64(2))
+    for h in (0, 5):
+        full = oracle.grads(qn[0, h][rows_late], kn[0, h], vn[0, h], gn[0, h][rows_late], q_pos=t_late, causal=True,
+                            key_grads=False)
+        flat = rng.choice(N * 512, size=256, replace=False)
+        jj, cc = flat // 512, sb - 512 + flat % 512
+        tok = jj + N * cc
+        share = oracle.grads(qn[0, h][rows_late], kn[0, h][tok], vn[0, h][tok], gn[0, h][rows_late], q_pos=t_late,
+                             k_pos=tok, causal=True, lse=full["lse"], delta=full["delta"])
+        sel_j, sel_c = torch.as_tensor(jj, device="cuda"), torch.as_tensor(cc, device="cuda")
+        gh.grad_close(gh.to_host_f64(dk[sel_j, 0, h, sel_c]), share["dk"], rtol, f"dk head {h}, 256 keys")
+        gh.grad_close(gh.to_host_f64(dv[sel_j, 0, h, sel_c]), share["dv"], rtol, f"dv head {h}, 256 keys")
     # identities per head
     dk_h = dk.double().sum(dim=(0, 3))[0]  # [H, D]: sum over positions and key rows
     dv_h = dv.double().sum(dim=(0, 3))[0]
@@ -334,7 +353,7 @@ def test_batch2_gqa4_ring_forward_and_backward(lay):
     assert np.max(np.abs(gh.to_host_f64(lse_full)[..., 0] - want_lse)) <= gh.TOL["bf16"]["lse"]
     want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
     for name, got, ref in zip(("dq", "dk", "dv"), grads, want):
-        _close(gh.to_host_f64(got), ref, 2e-2, name)
+        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name)
 
 
 @pytest.mark.timeout(900)
@@ -366,5 +385,7 @@ def test_backward_identical_keys_closed_form_at_scale():
     for h in range(H):
         g = ra_inputs.bf16_to_f32(gn[0, h]).astype(np.float64) * inv[:, None]
         want_dv = np.cumsum(g[::-1], axis=0)[::-1]
-        _close(gh.to_host_f64(full["dv"][0, h]), want_dv, 2e-2, f"dv head {h}")
+        gh.grad_close(gh.to_host_f64(full["dv"][0, h]), want_dv, gh.GRAD_RTOL["bf16"], f"dv head {h}")
+        # dQ is zero exactly; what remains is rounding noise of the dS terms,
+        # each about 2^-8 of |dS| <= 12 / (t + 1) times scale |k0|: an absolute bound
         _close(gh.to_host_f64(full["dq"][0, h]), np.zeros((S, D)), 2e-2, f"dq head {h}")
