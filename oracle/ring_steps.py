@@ -32,27 +32,32 @@ def _visit(i, step, n, order):
 def ring_no_max(q, k, v, n_dev, visit_order=None, scale=None, dtype=np.float64):
     """Non-causal ring over contiguous blocks, plain exp sums (no running max).
 
-    q, k, v: [S, d].  Arithmetic in ``dtype`` (fp64 by default; fp32 reproduces
-    the pages' single-precision demonstration).  Returns (out [S, d], shape of
-    the largest score block any device formed).
+    What the ring computes, stated as one reduction: the sequence is cut into
+    N equal blocks; after s hops device i holds key/value block (i - s) mod N
+    (or the block a permuted step order puts there), so over N hops every
+    device meets every block once.  Device i's output is the ratio of two sums
+    over the blocks in the order they arrive: of the exp-weighted values
+    exp(sigma q k^T) v and of the weights exp(sigma q k^T) themselves.  All
+    devices and all hops are evaluated at once as a grid of score blocks
+    [hop, device, query, key]; the sums over hops run in arrival order.
+
+    q, k, v: [S, d] with S a multiple of n_dev.  Arithmetic in ``dtype`` (fp64
+    by default; fp32 reproduces the pages' single-precision demonstration).
+    Returns (out [S, d], shape of one device's score block).
     """
     q, k, v = (np.asarray(a, dtype=dtype) for a in (q, k, v))
     S, d = q.shape
+    if S % n_dev:
+        raise ValueError("the sequence must split into equal blocks")
     sig = dtype(scale or 1.0 / np.sqrt(d))
-    qb, kb, vb = (np.array_split(a, n_dev) for a in (q, k, v))
-    per_device, largest = [], (0, 0)
-    for i in range(n_dev):
-        weighted = np.zeros((qb[i].shape[0], d), dtype=dtype)   # running sum of p v
-        total = np.zeros((qb[i].shape[0], 1), dtype=dtype)      # running sum of p
-        for step in range(n_dev):
-            j = _visit(i, step, n_dev, visit_order)
-            scores = (qb[i] @ kb[j].T) * sig
-            largest = max(largest, scores.shape)
-            p = np.exp(scores)
-            weighted += p @ vb[j]
-            total += p.sum(axis=-1, keepdims=True)
-        per_device.append(weighted / total)
-    return np.concatenate(per_device), largest
+    qb, kb, vb = (a.reshape(n_dev, S // n_dev, d) for a in (q, k, v))
+    offsets = np.arange(n_dev) if visit_order is None else np.asarray(visit_order)
+    held = (np.arange(n_dev)[None, :] - offsets[:, None]) % n_dev  # [hop, device]: block held
+    weights = np.exp(np.einsum("iqd,hikd->hiqk", qb, kb[held]) * sig)
+    weighted = np.einsum("hiqk,hikd->hiqd", weights, vb[held])
+    mass = weights.sum(axis=3)
+    out = np.cumsum(weighted, axis=0)[-1] / np.cumsum(mass, axis=0)[-1][..., None]
+    return out.reshape(S, d), weights.shape[2:]
 
 
 def block_partial(qi, qpos, kj, vj, kpos, causal, sig):
