@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define RA_ABI_VERSION 4
+#define RA_ABI_VERSION 5
 
 typedef enum ra_status {
     RA_OK = 0,
@@ -116,6 +116,17 @@ typedef struct ra_block_desc {
  */
 ra_status ra_block_attn_fwd(const ra_block_desc* desc, const void* q, const void* k,
                             const void* v, float* o, float* m, float* l, void* stream);
+/*
+ * ra_block_attn_fwd_kernel -- which kernel ra_block_attn_fwd would run for the
+ * same arguments, decided on the host with no GPU work: 1 = the bf16 MFMA
+ * kernel, 0 = the vector-ALU kernel (also for a valid empty call), -1 = the
+ * call would be rejected (ra_last_error says why).  The MFMA kernel needs
+ * bfloat16, head_dim 64 or 128, 16-byte aligned q, k, v, o, strides that are
+ * multiples of 8 elements, and key/value row strides below 2^24 elements.
+ */
+int32_t ra_block_attn_fwd_kernel(const ra_block_desc* desc, const void* q, const void* k, const void* v,
+                                 const float* o, const float* m, const float* l);
+
 /* With RA_BLOCK_ACCUMULATE, (o, m, l) hold a running state (a partial of some
  * other key set, in the same layout) on entry, and on return hold the merge of
  * that state with this block's partial -- the result ra_lse_merge would give
@@ -300,6 +311,15 @@ ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const
 ra_status ra_block_attn_bwd(const ra_block_desc* desc, const void* q, const void* k,
                             const void* v, const void* dout, const float* lse,
                             const float* delta, float* dq, float* dk, float* dv, void* stream);
+
+/* ra_block_attn_bwd_kernel -- which kernels ra_block_attn_bwd would run for
+ * the same arguments (host only): 1 = bf16 MFMA, 0 = vector ALU (also for a
+ * valid empty call), -1 = rejected.  MFMA needs bfloat16, head_dim 64 or 128,
+ * 16-byte aligned tensors, strides that are multiples of 8 elements and row
+ * strides below 2^24 elements. */
+int32_t ra_block_attn_bwd_kernel(const ra_block_desc* desc, const void* q, const void* k, const void* v,
+                                 const void* dout, const float* lse, const float* delta, const float* dq,
+                                 const float* dk, const float* dv);
 
 /* Bytes of device workspace ra_ring_backward needs (256-byte aligned base). */
 ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* desc, size_t* bytes);

@@ -59,7 +59,8 @@ class ra_ring_desc(ctypes.Structure):
 EXPORTS = ["ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ring_forward",
            "ra_stripe_permute", "ra_mask_offset", "ra_unmasked_pairs", "ra_ring_pair_offset",
            "ra_last_error", "ra_abi_version", "ra_release", "ra_attn_bwd_delta", "ra_block_attn_bwd",
-           "ra_ring_bwd_workspace_size", "ra_ring_backward"]
+           "ra_ring_bwd_workspace_size", "ra_ring_backward", "ra_block_attn_fwd_kernel",
+           "ra_block_attn_bwd_kernel"]
 
 _lib = None
 
@@ -105,6 +106,10 @@ def load_library(path: str = LIB_PATH):
     lib.ra_ring_backward.argtypes = [ctypes.POINTER(ra_ring_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      ctypes.c_size_t, vp]
     lib.ra_ring_backward.restype = ctypes.c_int
+    lib.ra_block_attn_fwd_kernel.argtypes = [ctypes.POINTER(ra_block_desc), vp, vp, vp, vp, vp, vp]
+    lib.ra_block_attn_fwd_kernel.restype = i32
+    lib.ra_block_attn_bwd_kernel.argtypes = [ctypes.POINTER(ra_block_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ra_block_attn_bwd_kernel.restype = i32
     del f32
     if path == LIB_PATH:
         _lib = lib

@@ -659,6 +659,10 @@ bool mfma_eligible(const BlockArgs& a, int dtype) {
     if (!aligned16(a.q) || !aligned16(a.k) || !aligned16(a.v) || !aligned16(a.o)) return false;
     for (int i = 0; i < 3; ++i)
         if (a.qs[i] % 8 || a.ks[i] % 8 || a.vs[i] % 8) return false;
+    // the tile copies address key/value rows by 32-bit per-lane byte offsets
+    // from the tile's base: row (< kNk) x row stride x 2 bytes must fit
+    const int64_t lim = int64_t(1) << 24;
+    if (a.ks[2] >= lim || a.vs[2] >= lim) return false;
     return true;
 }
 

@@ -60,7 +60,6 @@ bool valid_dtype(int32_t d) { return d == RA_F32 || d == RA_BF16; }
 bool aligned_to(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int64_t kMaxLen = (int64_t(1) << 31) - 1;
-constexpr int64_t kCUs = 256;  // compute units of an MI355X (8 XCDs x 32)
 
 // Shared shape checks of the block and ring descriptors.
 ra_status check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
@@ -89,6 +88,56 @@ ra_status launch_block(const ra::BlockArgs& a, int32_t dtype, uint32_t flags, hi
     else
         e = ra::launch_block_simt(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "block attention launch");
+    return RA_OK;
+}
+
+
+// Validates a forward block call and fills its kernel arguments.  q_len == 0
+// is valid (a no-op) and returns RA_OK with the arguments unset.
+ra_status block_fwd_args(const ra_block_desc* d, const void* q, const void* k, const void* v, float* o, float* m,
+                         float* l, ra::BlockArgs* out) {
+    if (!d) return fail(RA_ERR_INVALID, "null descriptor");
+    ra_status st = check_heads(d->batch, d->q_heads, d->kv_heads, d->head_dim, d->dtype);
+    if (st != RA_OK) return st;
+    if (d->q_len < 0 || d->kv_len < 0 || d->q_len > kMaxLen || d->kv_len > kMaxLen)
+        return fail(RA_ERR_INVALID, "q_len / kv_len out of range");
+    if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID, "causal must be 0 or 1");
+    if (d->flags & ~(RA_BLOCK_FORCE_SIMT | RA_BLOCK_ACCUMULATE))
+        return fail(RA_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+    if (d->pos_stride < 1) return fail(RA_ERR_INVALID, "pos_stride must be >= 1");
+    if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
+    for (int i = 0; i < 3; ++i)
+        if (d->q_strides[i] < 0 || d->k_strides[i] < 0 || d->v_strides[i] < 0)
+            return fail(RA_ERR_INVALID, "strides must be non-negative");
+    if (d->q_len == 0) return RA_OK;
+    if (!q || !o || !m || !l) return fail(RA_ERR_INVALID, "null q / o / m / l pointer");
+    if (d->kv_len > 0 && (!k || !v)) return fail(RA_ERR_INVALID, "null k / v pointer");
+    const size_t es = elem_size(d->dtype);
+    if (!aligned_to(q, es) || (k && !aligned_to(k, es)) || (v && !aligned_to(v, es)) || !aligned_to(o, 4) ||
+        !aligned_to(m, 4) || !aligned_to(l, 4))
+        return fail(RA_ERR_INVALID, "misaligned pointer");
+    ra::BlockArgs& a = *out;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.m = m;
+    a.l = l;
+    a.B = d->batch;
+    a.Hq = d->q_heads;
+    a.Hkv = d->kv_heads;
+    a.D = d->head_dim;
+    a.q_len = static_cast<int32_t>(d->q_len);
+    a.kv_len = static_cast<int32_t>(d->kv_len);
+    for (int i = 0; i < 3; ++i) {
+        a.qs[i] = d->q_strides[i];
+        a.ks[i] = d->k_strides[i];
+        a.vs[i] = d->v_strides[i];
+    }
+    a.scale = resolve_scale(d->scale, d->head_dim);
+    a.causal = d->causal;
+    a.mask_offset = clamp_offset(ra_mask_offset(d->q_pos0, d->k_pos0, d->pos_stride), d->q_len, d->kv_len);
+    a.accumulate = (d->flags & RA_BLOCK_ACCUMULATE) ? 1 : 0;
     return RA_OK;
 }
 
@@ -122,50 +171,18 @@ int32_t ra_abi_version(void) { return RA_ABI_VERSION; }
 
 ra_status ra_block_attn_fwd(const ra_block_desc* d, const void* q, const void* k, const void* v, float* o,
                             float* m, float* l, void* stream) {
-    if (!d) return fail(RA_ERR_INVALID, "null descriptor");
-    ra_status st = check_heads(d->batch, d->q_heads, d->kv_heads, d->head_dim, d->dtype);
-    if (st != RA_OK) return st;
-    if (d->q_len < 0 || d->kv_len < 0 || d->q_len > kMaxLen || d->kv_len > kMaxLen)
-        return fail(RA_ERR_INVALID, "q_len / kv_len out of range");
-    if (d->causal != 0 && d->causal != 1) return fail(RA_ERR_INVALID, "causal must be 0 or 1");
-    if (d->flags & ~(RA_BLOCK_FORCE_SIMT | RA_BLOCK_ACCUMULATE))
-        return fail(RA_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
-    if (d->pos_stride < 1) return fail(RA_ERR_INVALID, "pos_stride must be >= 1");
-    if (!std::isfinite(d->scale)) return fail(RA_ERR_INVALID, "scale must be finite");
-    for (int i = 0; i < 3; ++i)
-        if (d->q_strides[i] < 0 || d->k_strides[i] < 0 || d->v_strides[i] < 0)
-            return fail(RA_ERR_INVALID, "strides must be non-negative");
-    if (d->q_len == 0) return RA_OK;
-    if (!q || !o || !m || !l) return fail(RA_ERR_INVALID, "null q / o / m / l pointer");
-    if (d->kv_len > 0 && (!k || !v)) return fail(RA_ERR_INVALID, "null k / v pointer");
-    const size_t es = elem_size(d->dtype);
-    if (!aligned_to(q, es) || (k && !aligned_to(k, es)) || (v && !aligned_to(v, es)) || !aligned_to(o, 4) ||
-        !aligned_to(m, 4) || !aligned_to(l, 4))
-        return fail(RA_ERR_INVALID, "misaligned pointer");
-
     ra::BlockArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.m = m;
-    a.l = l;
-    a.B = d->batch;
-    a.Hq = d->q_heads;
-    a.Hkv = d->kv_heads;
-    a.D = d->head_dim;
-    a.q_len = static_cast<int32_t>(d->q_len);
-    a.kv_len = static_cast<int32_t>(d->kv_len);
-    for (int i = 0; i < 3; ++i) {
-        a.qs[i] = d->q_strides[i];
-        a.ks[i] = d->k_strides[i];
-        a.vs[i] = d->v_strides[i];
-    }
-    a.scale = resolve_scale(d->scale, d->head_dim);
-    a.causal = d->causal;
-    a.mask_offset = clamp_offset(ra_mask_offset(d->q_pos0, d->k_pos0, d->pos_stride), d->q_len, d->kv_len);
-    a.accumulate = (d->flags & RA_BLOCK_ACCUMULATE) ? 1 : 0;
+    const ra_status st = block_fwd_args(d, q, k, v, o, m, l, &a);
+    if (st != RA_OK || d->q_len == 0) return st;
     return launch_block(a, d->dtype, d->flags, static_cast<hipStream_t>(stream));
+}
+
+int32_t ra_block_attn_fwd_kernel(const ra_block_desc* d, const void* q, const void* k, const void* v,
+                                 const float* o, const float* m, const float* l) {
+    ra::BlockArgs a{};
+    if (block_fwd_args(d, q, k, v, const_cast<float*>(o), const_cast<float*>(m), const_cast<float*>(l), &a) != RA_OK)
+        return -1;
+    return (!(d->flags & RA_BLOCK_FORCE_SIMT) && ra::mfma_eligible(a, d->dtype)) ? 1 : 0;
 }
 
 ra_status ra_lse_merge(int64_t rows, int32_t head_dim, float* o_acc, float* m_acc, float* l_acc,
@@ -283,9 +300,10 @@ RingGeometry geometry(const ra_ring_desc* d) {
         const int64_t tiles = (Sb + ra::mfma_key_tile() - 1) / ra::mfma_key_tile();
         int64_t want = d->kv_splits;
         if (want == 0) {  // automatic: about one workgroup per compute unit, >= 2 key tiles per range
+            const int64_t cus = ra::compute_units();
             const int64_t wg = (Sb + ra::mfma_query_tile() - 1) / ra::mfma_query_tile() * d->q_heads * d->batch *
                                std::min(g.n_streams, d->n_run);
-            want = wg >= kCUs ? 1 : std::min<int64_t>((kCUs + wg - 1) / wg, tiles / 2);
+            want = wg >= cus ? 1 : std::min<int64_t>((cus + wg - 1) / wg, tiles / 2);
         }
         want = std::max<int64_t>(1, std::min<int64_t>({want, tiles, ra::kMaxMergeParts}));
         if (want > 1) {
@@ -674,8 +692,13 @@ ra_status ra_attn_bwd_delta(int64_t rows, int32_t head_dim, int32_t dtype, const
     return RA_OK;
 }
 
-ra_status ra_block_attn_bwd(const ra_block_desc* d, const void* q, const void* k, const void* v, const void* dout,
-                            const float* lse, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+namespace {
+// Validates a backward block call and fills its kernel arguments; *empty is
+// set when the call is a valid no-op (q_len or kv_len zero).
+ra_status block_bwd_args(const ra_block_desc* d, const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, float* dq, float* dk, float* dv, ra::BwdArgs* out,
+                         bool* empty) {
+    *empty = false;
     if (!d) return fail(RA_ERR_INVALID, "null descriptor");
     ra_status st = check_heads(d->batch, d->q_heads, d->kv_heads, d->head_dim, d->dtype);
     if (st != RA_OK) return st;
@@ -688,14 +711,17 @@ ra_status ra_block_attn_bwd(const ra_block_desc* d, const void* q, const void* k
     for (int i = 0; i < 3; ++i)
         if (d->q_strides[i] < 0 || d->k_strides[i] < 0 || d->v_strides[i] < 0)
             return fail(RA_ERR_INVALID, "strides must be non-negative");
-    if (d->q_len == 0 || d->kv_len == 0) return RA_OK;
+    if (d->q_len == 0 || d->kv_len == 0) {
+        *empty = true;
+        return RA_OK;
+    }
     if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv)
         return fail(RA_ERR_INVALID, "null pointer");
     const size_t es = elem_size(d->dtype);
     if (!aligned_to(q, es) || !aligned_to(k, es) || !aligned_to(v, es) || !aligned_to(dout, es) ||
         !aligned_to(lse, 4) || !aligned_to(delta, 4) || !aligned_to(dq, 4) || !aligned_to(dk, 4) || !aligned_to(dv, 4))
         return fail(RA_ERR_INVALID, "misaligned pointer");
-    ra::BwdArgs a{};
+    ra::BwdArgs& a = *out;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -720,9 +746,31 @@ ra_status ra_block_attn_bwd(const ra_block_desc* d, const void* q, const void* k
     a.scale = resolve_scale(d->scale, d->head_dim);
     a.causal = d->causal;
     a.mask_offset = clamp_offset(ra_mask_offset(d->q_pos0, d->k_pos0, d->pos_stride), d->q_len, d->kv_len);
+    return RA_OK;
+}
+}  // namespace
+
+ra_status ra_block_attn_bwd(const ra_block_desc* d, const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, float* dq, float* dk, float* dv, void* stream) {
+    ra::BwdArgs a{};
+    bool empty = false;
+    const ra_status st = block_bwd_args(d, q, k, v, dout, lse, delta, dq, dk, dv, &a, &empty);
+    if (st != RA_OK || empty) return st;
     const hipError_t e = ra::launch_block_bwd(a, d->dtype, d->flags & RA_BLOCK_FORCE_SIMT, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "block backward launch");
     return RA_OK;
+}
+
+int32_t ra_block_attn_bwd_kernel(const ra_block_desc* d, const void* q, const void* k, const void* v,
+                                 const void* dout, const float* lse, const float* delta, const float* dq,
+                                 const float* dk, const float* dv) {
+    ra::BwdArgs a{};
+    bool empty = false;
+    if (block_bwd_args(d, q, k, v, dout, lse, delta, const_cast<float*>(dq), const_cast<float*>(dk),
+                       const_cast<float*>(dv), &a, &empty) != RA_OK)
+        return -1;
+    if (empty) return 0;
+    return (!(d->flags & RA_BLOCK_FORCE_SIMT) && ra::bwd_mfma_eligible(a, d->dtype)) ? 1 : 0;
 }
 
 ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* d, size_t* bytes) {

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     for name in names:
         assert hasattr(lib, name), f"libra.so does not export {name}"
     assert set(names) == set(B.EXPORTS)
-    assert lib.ra_abi_version() == 4
+    assert lib.ra_abi_version() == 5
 
 
 def test_mask_offset_is_floor_division(lib):
@@ -238,3 +238,55 @@ def test_backward_validation(lib):
     assert n.value == 32 * 32768 * 4  # one delta per row of the run position
     st = lib.ra_ring_backward(ctypes.byref(r), *([FAKE] * 9), ctypes.c_void_p(0x100000), 1024, None)
     assert st == B.RA_ERR_WORKSPACE
+
+
+def _desc(D=128, dtype=B.RA_BF16, q_len=256, kv_len=256, kv_row_stride=None, flags=0):
+    d = B.ra_block_desc()
+    d.batch, d.q_heads, d.kv_heads, d.head_dim = 1, 2, 1, D
+    d.q_len, d.kv_len = q_len, kv_len
+    d.dtype, d.causal, d.scale, d.flags = dtype, 1, 0.0, flags
+    d.q_pos0, d.k_pos0, d.pos_stride = 0, 0, 1
+    rs = D if kv_row_stride is None else kv_row_stride
+    d.q_strides[:] = [2 * q_len * D, q_len * D, D]
+    d.k_strides[:] = [kv_len * rs, kv_len * rs, rs]
+    d.v_strides[:] = [kv_len * rs, kv_len * rs, rs]
+    return d
+
+
+def test_block_kernel_selection_on_host(lib):
+    """Which kernel a block call would run, decided on the host: bf16 with head_dim
+    64 or 128 takes the MFMA kernels; fp32, other head_dims, the force flag,
+    misalignment and key/value row strides of 2^24 elements or more (whose
+    per-lane 32-bit copy offsets would wrap) take the vector-ALU kernels; invalid
+    calls return -1.  No pointer is dereferenced (no kernel is launched)."""
+    a16 = ctypes.c_void_p(0x100000)   # 16-byte aligned fake device addresses
+    odd = ctypes.c_void_p(0x100008)   # 8-byte aligned only
+
+    def fwd(d, q=a16, o=a16):
+        return lib.ra_block_attn_fwd_kernel(ctypes.byref(d), q, a16, a16, o, a16, a16)
+
+    def bwd(d, q=a16):
+        return lib.ra_block_attn_bwd_kernel(ctypes.byref(d), q, a16, a16, a16, a16, a16, a16, a16, a16)
+
+    assert fwd(_desc(128)) == 1 and bwd(_desc(128)) == 1
+    assert fwd(_desc(64)) == 1 and bwd(_desc(64)) == 1
+    assert fwd(_desc(96)) == 0 and bwd(_desc(96)) == 0
+    assert fwd(_desc(128, dtype=B.RA_F32)) == 0 and bwd(_desc(128, dtype=B.RA_F32)) == 0
+    assert fwd(_desc(128, flags=B.RA_BLOCK_FORCE_SIMT)) == 0
+    assert bwd(_desc(128, flags=B.RA_BLOCK_FORCE_SIMT)) == 0
+    assert fwd(_desc(128), q=odd) == 0 and bwd(_desc(128), q=odd) == 0
+    # row strides: the largest that keeps 32-bit copy offsets, and the first that does not
+    assert fwd(_desc(128, kv_row_stride=(1 << 24) - 8)) == 1
+    assert fwd(_desc(128, kv_row_stride=1 << 24)) == 0
+    assert bwd(_desc(128, kv_row_stride=(1 << 24) - 8)) == 1
+    assert bwd(_desc(128, kv_row_stride=1 << 24)) == 0
+    # a stride that is not a multiple of 8 elements (16-byte rows) stays off MFMA
+    assert fwd(_desc(128, kv_row_stride=136 + 4)) == 0
+    # empty calls are valid no-ops; invalid ones are rejected with a message
+    assert fwd(_desc(128, q_len=0), q=FAKE) == 0
+    assert bwd(_desc(128, kv_len=0)) == 0
+    bad = _desc(128)
+    bad.pos_stride = 0
+    assert fwd(bad) == -1 and b"pos_stride" in lib.ra_last_error()
+    assert bwd(bad) == -1
+    assert lib.ra_block_attn_fwd_kernel(None, a16, a16, a16, a16, a16, a16) == -1
