@@ -39,6 +39,13 @@ def _close(got, want, tol, what):
     return err / ref
 
 
+def _dq_delta_extra(qn, kn, vn, gn, causal):
+    """dq_delta_bound over whole [B, Hq, S, D] tensors: the oracle's O and P K."""
+    o_ref, _ = oracle.attention(qn, kn, vn, causal=causal)
+    pk_ref, _ = oracle.attention(qn, kn, kn, causal=causal)
+    return gh.dq_delta_bound(o_ref, pk_ref, gn, 1.0 / np.sqrt(qn.shape[-1]))
+
+
 def test_delta_kernel():
     for dtype, D in (("f32", 48), ("bf16", 128)):
         gh.say("ra_attn_bwd_delta", dtype, D)
@@ -196,10 +203,12 @@ def test_ring_backward_matches_oracle(lay, causal, dtype, D, N, S):
     torch.cuda.synchronize()
     want = oracle.attention_grads(qn, kn, vn, gn, causal=causal)
     # the backward consumes the GPU forward's bf16 output and fp32 lse, so bf16
-    # rings carry that rounding too
+    # rings carry that rounding too (in dQ through delta = dO . O)
     tol = gh.GRAD_RTOL["bf16"] if dtype == "bf16" else gh.GRAD_RTOL["fp32"]
-    for name, got, ref in (("dq", dq_g, want[0]), ("dk", dk_g, want[1]), ("dv", dv_g, want[2])):
-        gh.grad_close(gh.to_host_f64(got), ref, tol, name)
+    extra = _dq_delta_extra(qn, kn, vn, gn, causal) if dtype == "bf16" else None
+    for name, got, ref, ex in (("dq", dq_g, want[0], extra), ("dk", dk_g, want[1], None),
+                               ("dv", dv_g, want[2], None)):
+        gh.grad_close(gh.to_host_f64(got), ref, tol, name, extra=ex)
 
 
 def test_mfma_backward_runs_and_differs_from_vector_path():
@@ -251,8 +260,9 @@ def test_ring_backward_gqa_moderate_size_all_gradients():
         outs.append(full)
     torch.cuda.synchronize()
     want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
-    for name, got, ref in zip(("dq", "dk", "dv"), outs, want):
-        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name)
+    extras = (_dq_delta_extra(qn, kn, vn, gn, True), None, None)
+    for name, got, ref, ex in zip(("dq", "dk", "dv"), outs, want, extras):
+        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name, extra=ex)
 
 
 @pytest.mark.timeout(900)
@@ -291,12 +301,17 @@ def test_backward_256k_share_sampled_rows_and_identities():
     rr = (stt - i) // N
     got = gh.to_host_f64(dq[0, 0][torch.as_tensor(sh, device="cuda"), torch.as_tensor(rr, device="cuda")])
     want = np.empty_like(got)
+    o_ref = np.empty_like(got)
+    pk_ref = np.empty_like(got)
     for h in np.unique(sh):
         idx = np.nonzero(sh == h)[0]
         r = oracle.grads(qn[0, h][rr[idx]], kn[0, h], vn[0, h], gn[0, h][rr[idx]], q_pos=stt[idx], causal=True,
                          key_grads=False)
         want[idx] = r["dq"]
-    gh.grad_close(got, want, rtol, "dq, 1024 sampled share rows")
+        o_ref[idx] = oracle.rows(qn[0, h][rr[idx]], kn[0, h], vn[0, h], q_pos=stt[idx], causal=True)["o"]
+        pk_ref[idx] = oracle.rows(qn[0, h][rr[idx]], kn[0, h], kn[0, h], q_pos=stt[idx], causal=True)["o"]
+    extra = gh.dq_delta_bound(o_ref, pk_ref, gn[0][sh, rr], 1.0 / np.sqrt(D))
+    gh.grad_close(got, want, rtol, "dq, 1024 sampled share rows", extra=extra)
     # dK, dV: sampled keys of the last 4096 tokens, every block j (local rows c >= sb - 512)
     rows_late = np.arange(sb - 512, sb)
     t_late = i + N * rows_late
@@ -352,8 +367,9 @@ def test_batch2_gqa4_ring_forward_and_backward(lay):
     assert np.max(np.abs(gh.to_host_f64(o_full) - want_o)) <= gh.TOL["bf16"]["o"]
     assert np.max(np.abs(gh.to_host_f64(lse_full)[..., 0] - want_lse)) <= gh.TOL["bf16"]["lse"]
     want = oracle.attention_grads(qn, kn, vn, gn, causal=True)
-    for name, got, ref in zip(("dq", "dk", "dv"), grads, want):
-        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name)
+    extras = (_dq_delta_extra(qn, kn, vn, gn, True), None, None)
+    for name, got, ref, ex in zip(("dq", "dk", "dv"), grads, want, extras):
+        gh.grad_close(gh.to_host_f64(got), ref, gh.GRAD_RTOL["bf16"], name, extra=ex)
 
 
 @pytest.mark.timeout(900)
