@@ -259,6 +259,31 @@ ra_status ra_ring_forward(const ra_ring_desc* desc, const void* q, const void* k
                           void* stream);
 
 /*
+ * ra_ring_forward_noalloc -- ra_ring_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts and results as
+ * ra_ring_forward with n_streams = 1, without the workspace: the scratch
+ * (running states, key-range partials, tile-queue counters) is a device array
+ * the library holds, ra_ring_noalloc_max_bytes() bytes (256 MiB: enough for
+ * one position's share of the 256K-token, 8-head, head_dim 128 ring) per GPU,
+ * from the first call on that GPU until the process ends: that first call
+ * looks the array's address up, and the HIP runtime backs it with device
+ * memory then (make it before capture or a no-allocation section begins).
+ * Every later call creates no stream, event or device memory; every launch
+ * goes to `stream`, in order.
+ * Refused before anything is launched: desc->stats or desc->emulate_copy
+ * (RA_ERR_UNSUPPORTED, they need library events and streams), and shapes
+ * whose scratch (ra_ring_workspace_size with n_streams = 1) exceeds the array
+ * (RA_ERR_WORKSPACE).  Every call on one GPU shares that GPU's array and
+ * leaves its last contents there; calls whose GPU work may overlap on one GPU
+ * (other streams, other threads) race on it and give wrong results.
+ */
+ra_status ra_ring_forward_noalloc(const ra_ring_desc* desc, const void* q, const void* k, const void* v,
+                                  void* o, float* lse, void* stream);
+/* Bytes of scratch ra_ring_forward_noalloc holds per GPU. */
+size_t ra_ring_noalloc_max_bytes(void);
+
+/*
  * ra_stripe_permute -- build (or undo) the per-position shard layout: the
  * contiguous split of the pages' ring (N equal blocks) or the striped layout
  * ("Ring Attention", section "How ring attention works": each position gets

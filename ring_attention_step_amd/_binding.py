@@ -60,7 +60,7 @@ EXPORTS = ["ra_block_attn_fwd", "ra_lse_merge", "ra_ring_workspace_size", "ra_ri
            "ra_stripe_permute", "ra_mask_offset", "ra_unmasked_pairs", "ra_ring_pair_offset",
            "ra_last_error", "ra_abi_version", "ra_release", "ra_attn_bwd_delta", "ra_block_attn_bwd",
            "ra_ring_bwd_workspace_size", "ra_ring_backward", "ra_block_attn_fwd_kernel",
-           "ra_block_attn_bwd_kernel"]
+           "ra_block_attn_bwd_kernel", "ra_ring_forward_noalloc", "ra_ring_noalloc_max_bytes"]
 
 _lib = None
 
@@ -110,6 +110,10 @@ def load_library(path: str = LIB_PATH):
     lib.ra_block_attn_fwd_kernel.restype = i32
     lib.ra_block_attn_bwd_kernel.argtypes = [ctypes.POINTER(ra_block_desc), vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ra_block_attn_bwd_kernel.restype = i32
+    lib.ra_ring_forward_noalloc.argtypes = [ctypes.POINTER(ra_ring_desc), vp, vp, vp, vp, vp, vp]
+    lib.ra_ring_forward_noalloc.restype = ctypes.c_int
+    lib.ra_ring_noalloc_max_bytes.argtypes = []
+    lib.ra_ring_noalloc_max_bytes.restype = ctypes.c_size_t
     del f32
     if path == LIB_PATH:
         _lib = lib
@@ -282,6 +286,25 @@ def ra_ring_forward(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contigu
     if st is None:
         return None
     return {name: getattr(st, name) for name, _ in ra_ring_stats._fields_}
+
+
+def ra_ring_forward_noalloc(q, k, v, o, lse=None, *, n_pos, first_pos=0, layout="contiguous", causal=False,
+                            scale=0.0, separate_merge=False, kv_splits=0, visit_order=None, stream=None):
+    """ra_ring_forward on one stream (the current one) with the library's own
+    device scratch: the call allocates nothing, on the device or through torch."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need_dense(t, name)
+    _need_dense(lse, "lse", torch.float32)
+    if v.shape != k.shape or o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("v must match k and o must match q")
+    d = ring_desc(q, k, n_pos=n_pos, first_pos=first_pos, layout=layout, causal=causal, scale=scale,
+                  n_streams=1, separate_merge=separate_merge, kv_splits=kv_splits, visit_order=visit_order)
+    _check(load_library().ra_ring_forward_noalloc(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                  _stream(stream)))
+
+
+def ra_ring_noalloc_max_bytes() -> int:
+    return load_library().ra_ring_noalloc_max_bytes()
 
 
 def ra_stripe_permute(x, y, *, layout, inverse, n_pos, stream=None):

@@ -398,8 +398,16 @@ ra_status ra_ring_workspace_size(const ra_ring_desc* d, size_t* bytes) {
     return RA_OK;
 }
 
-ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The ring forward.  own_streams: positions run on library-owned streams
+// forked from and joined back to `stream` with events (created on first use);
+// otherwise every launch goes to `stream` itself, in order, and no stream or
+// event is created or recorded (stats and emulate_copy must then be off).
+ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, const void* v, void* o,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream, bool own_streams) {
     ra_status st = check_ring(d);
     if (st != RA_OK) return st;
     if (!q || !k || !v || !o) return fail(RA_ERR_INVALID, "null q / k / v / o pointer");
@@ -471,20 +479,27 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
     stats.flops = 4.0 * D * stats.unmasked_pairs;
     stats.kv_splits = 1;
 
+    if (!own_streams && (d->stats || d->emulate_copy))
+        return fail(RA_ERR_UNSUPPORTED, "stats and emulate_copy need library streams and events");
     std::lock_guard<std::mutex> lock(g_mutex);
     int dev = 0;
     RA_HIP(hipGetDevice(&dev));
-    DeviceState& ds = g_devices[dev];
-    st = ensure_streams(ds, g.n_streams);
-    if (st != RA_OK) return st;
-    // sync events: fork, per-stream join, per (position, parity) copied / used
-    const size_t n_sync = 1 + g.n_streams + 4 * static_cast<size_t>(d->n_run);
-    st = ensure_events(ds.sync_events, n_sync, hipEventDisableTiming);
-    if (st != RA_OK) return st;
-    hipEvent_t ev_fork = ds.sync_events[0];
+    DeviceState no_state;
+    DeviceState& ds = own_streams ? g_devices[dev] : no_state;
+    if (own_streams) {
+        st = ensure_streams(ds, g.n_streams);
+        if (st != RA_OK) return st;
+        // sync events: fork, per-stream join, per (position, parity) copied / used
+        const size_t n_sync = 1 + g.n_streams + 4 * static_cast<size_t>(d->n_run);
+        st = ensure_events(ds.sync_events, n_sync, hipEventDisableTiming);
+        if (st != RA_OK) return st;
+    }
+    auto ev_fork = [&]() { return ds.sync_events[0]; };
     auto ev_join = [&](int s) { return ds.sync_events[1 + s]; };
     auto ev_copied = [&](int p, int par) { return ds.sync_events[1 + g.n_streams + 4 * p + par]; };
     auto ev_used = [&](int p, int par) { return ds.sync_events[1 + g.n_streams + 4 * p + 2 + par]; };
+    // the stream position p's work (and the queue counters of stream slot s) run on
+    auto compute_stream = [&](int s) { return own_streams ? ds.compute[s] : caller; };
 
     Timer timer;
     if (d->stats) timer.pool = &ds.timing_events;
@@ -497,16 +512,18 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
                                  d->batch * g.n_splits;
     const bool use_queue = launch_tiles >= 2 * static_cast<int64_t>(ra::compute_units());
 
-    RA_HIP(hipEventRecord(ev_fork, caller));
+    if (own_streams) RA_HIP(hipEventRecord(ev_fork(), caller));
     for (int s = 0; s < g.n_streams; ++s) {
-        RA_HIP(hipStreamWaitEvent(ds.compute[s], ev_fork, 0));
-        if (d->emulate_copy) RA_HIP(hipStreamWaitEvent(ds.copy[s], ev_fork, 0));
+        if (own_streams) {
+            RA_HIP(hipStreamWaitEvent(ds.compute[s], ev_fork(), 0));
+            if (d->emulate_copy) RA_HIP(hipStreamWaitEvent(ds.copy[s], ev_fork(), 0));
+        }
         // the stream's tile-queue counters start at zero (each block launch
         // leaves them so); a fill kernel, not a memset, so that the call can be
         // captured in a graph
         if (use_queue) {
             const hipError_t e = ra::launch_fill_zero(reinterpret_cast<float*>(part[s].queue),
-                                                      static_cast<int64_t>(g.queue / 4), ds.compute[s]);
+                                                      static_cast<int64_t>(g.queue / 4), compute_stream(s));
             if (e != hipSuccess) return hip_fail(e, "queue reset launch");
         }
     }
@@ -546,7 +563,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         for (int p = 0; p < d->n_run; ++p) {
             const RingPlanStep& ps = plan[p][s];
             const int sid = p % g.n_streams;
-            const hipStream_t cs = ds.compute[sid];
+            const hipStream_t cs = compute_stream(sid);
             const int par = s & 1;
             const void* kp = kb + static_cast<size_t>(ps.block) * kv_bytes;
             const void* vp = vb + static_cast<size_t>(ps.block) * kv_bytes;
@@ -646,7 +663,7 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         }
     }
 
-    for (int s = 0; s < g.n_streams; ++s) {
+    for (int s = 0; s < g.n_streams && own_streams; ++s) {
         if (d->emulate_copy) {
             // the copy stream's tail must also be joined before the caller reuses the slots
             RA_HIP(hipEventRecord(ev_join(s), ds.copy[s]));
@@ -675,6 +692,24 @@ ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, c
         *d->stats = stats;
     }
     return RA_OK;
+}
+
+}  // namespace
+
+namespace ra {
+ra_status set_error(ra_status s, const char* msg) { return fail(s, "%s", msg); }
+
+ra_status ring_forward_on_stream(const ra_ring_desc* d, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    return ring_forward_run(d, q, k, v, o, lse, workspace, workspace_bytes, stream, false);
+}
+}  // namespace ra
+
+extern "C" {
+
+ra_status ra_ring_forward(const ra_ring_desc* d, const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return ring_forward_run(d, q, k, v, o, lse, workspace, workspace_bytes, stream, true);
 }
 
 // ------------------------------------------------------------------ backward

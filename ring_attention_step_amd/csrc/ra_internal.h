@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+
+#include "ra.h"
 #include <cstdint>
 
 namespace ra {
@@ -115,5 +117,14 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s);
 // Row moves between [BH, S, row] and [N, BH, S/N, row] under a token map.
 hipError_t launch_stripe_permute(int layout, int inverse, int64_t BH, int64_t S, int32_t N,
                                  int64_t row_bytes, const void* x, void* y, hipStream_t s);
+
+// Records a message for ra_last_error() and returns s.
+ra_status set_error(ra_status s, const char* msg);
+
+// The ring forward with every launch on `stream` itself: no library stream or
+// event is created or recorded (stats and emulate_copy are refused).  Same
+// arguments and workspace layout as ra_ring_forward with n_streams = 1.
+ra_status ring_forward_on_stream(const ra_ring_desc* d, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 }  // namespace ra
