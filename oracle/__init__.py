@@ -32,7 +32,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libra_oracle.so")
+# RA_ORACLE_LIBRARY names another build of attention_oracle.c (e.g. one with
+# sanitizers); by default the in-tree libra_oracle.so
+_SO = os.environ.get("RA_ORACLE_LIBRARY") or os.path.join(_HERE, "libra_oracle.so")
 _lib = None
 
 F32, BF16 = 0, 1

@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libra.so")
+# RA_LIBRARY names another build of the same library (e.g. one with host-side
+# sanitizers); by default the in-tree libra.so
+LIB_PATH = os.environ.get("RA_LIBRARY") or os.path.join(_HERE, "libra.so")
 
 RA_OK, RA_ERR_INVALID, RA_ERR_UNSUPPORTED, RA_ERR_HIP, RA_ERR_WORKSPACE = range(5)
 RA_F32, RA_BF16 = 0, 1
