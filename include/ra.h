@@ -354,9 +354,12 @@ ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * Steps run in lockstep as on a real ring: at step s position i holds block
  * j = (i - visit_order[s]) mod n_pos (distinct across positions) and adds its
  * share into its own dq and into the block's dk, dv.  Fully masked pairs are
- * skipped.  All work runs on `stream`; emulate_copy, n_streams and
- * separate_merge are ignored.  With desc->stats, backward launches are timed
- * (block_ms, block_launches) and flops counts the five products.
+ * skipped.  The positions of one step write disjoint outputs and run on
+ * n_streams library streams (0: min(n_run, 8); position p on stream p mod
+ * n_streams), forked from `stream` before each step and joined back to it
+ * after; emulate_copy and separate_merge are ignored.  With desc->stats,
+ * backward launches are timed (block_ms, block_launches; spans of launches on
+ * different streams may overlap) and flops counts the five products.
  *
  * q, o, dout: [n_run, batch, q_heads, Sb, head_dim] in dtype (o and lse from
  *   ra_ring_forward on the same desc);  lse: [n_run, batch, q_heads, Sb];

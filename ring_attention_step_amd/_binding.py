@@ -365,7 +365,8 @@ def ra_ring_bwd_workspace_size(desc) -> int:
 
 
 def ra_ring_backward(q, k, v, o, dout, lse, dq, dk, dv, *, n_pos, first_pos=0, layout="contiguous",
-                     causal=False, scale=0.0, visit_order=None, workspace=None, stats=False, stream=None):
+                     causal=False, scale=0.0, visit_order=None, n_streams=0, workspace=None, stats=False,
+                     stream=None):
     """Gradients of the ring: dq [n_run,B,Hq,Sb,D], dk, dv [n_pos,B,Hkv,Sb,D] (fp32, overwritten).
 
     Returns a dict of ra_ring_stats when stats=True, else None.
@@ -380,7 +381,7 @@ def ra_ring_backward(q, k, v, o, dout, lse, dq, dk, dv, *, n_pos, first_pos=0, l
         raise ValueError("dk, dv must match k; lse must be q's shape without head_dim")
     st = ra_ring_stats() if stats else None
     d = ring_desc(q, k, n_pos=n_pos, first_pos=first_pos, layout=layout, causal=causal, scale=scale,
-                  visit_order=visit_order, stats=st)
+                  visit_order=visit_order, n_streams=n_streams, stats=st)
     need = ra_ring_bwd_workspace_size(d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

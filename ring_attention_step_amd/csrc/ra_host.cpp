@@ -339,6 +339,7 @@ struct DeviceState {
     std::vector<hipStream_t> compute, copy;
     std::vector<hipEvent_t> sync_events;    // timing disabled
     std::vector<hipEvent_t> timing_events;  // timing enabled
+    std::vector<hipEvent_t> bwd_events;     // timing disabled: the ring backward's per-step fork and join
 };
 
 std::mutex g_mutex;
@@ -861,6 +862,17 @@ ra_status ra_ring_backward(const ra_ring_desc* d, const void* q, const void* k, 
     DeviceState& ds = g_devices[dev];
     Timer timer;
     if (d->stats) timer.pool = &ds.timing_events;
+    // the positions of one step write disjoint dq and dk / dv, so they run on
+    // n_streams library streams, forked from the caller's stream before every
+    // step and joined back after it (the next step hands every block to
+    // another position)
+    const int n_streams = d->n_streams > 0 ? std::min(d->n_streams, d->n_run) : std::min(d->n_run, 8);
+    if (n_streams > 1) {
+        st = ensure_streams(ds, n_streams);
+        if (st != RA_OK) return st;
+        st = ensure_events(ds.bwd_events, 1 + static_cast<size_t>(n_streams), hipEventDisableTiming);
+        if (st != RA_OK) return st;
+    }
 
     // gradients start at zero (fill kernels: no memset nodes under graph capture)
     hipError_t e = ra::launch_fill_zero(dq, static_cast<int64_t>(d->n_run) * q_elems, caller);
@@ -872,11 +884,16 @@ ra_status ra_ring_backward(const ra_ring_desc* d, const void* q, const void* k, 
     // Lockstep over steps, as on a real ring: at step s position i holds block
     // j = (i - visit[s]) mod N, distinct across positions, and adds its share
     // into that block's dK, dV (which travel with the block) and into its own
-    // dQ.  All launches go to the caller's stream in that order.
+    // dQ.  Position p's launches go to stream p mod n_streams.
     for (int32_t s = 0; s < N; ++s) {
+        if (n_streams > 1) {
+            RA_HIP(hipEventRecord(ds.bwd_events[0], caller));
+            for (int i = 0; i < n_streams; ++i) RA_HIP(hipStreamWaitEvent(ds.compute[i], ds.bwd_events[0], 0));
+        }
         for (int p = 0; p < d->n_run; ++p) {
             const RingPlanStep& ps = plan[p][s];
             if (ps.skip) continue;
+            const hipStream_t ps_stream = n_streams > 1 ? ds.compute[p % n_streams] : caller;
             ra::BwdArgs a{};
             const char* qb = static_cast<const char*>(q) + static_cast<size_t>(p) * q_elems * es;
             a.q = qb;
@@ -905,12 +922,18 @@ ra_status ra_ring_backward(const ra_ring_desc* d, const void* q, const void* k, 
             a.causal = d->causal;
             a.mask_offset = clamp_offset(ps.offset, Sb, Sb);
             size_t ti = 0;
-            st = timer.begin(caller, ti);
+            st = timer.begin(ps_stream, ti);
             if (st != RA_OK) return st;
-            e = ra::launch_block_bwd(a, d->dtype, 0, caller);
+            e = ra::launch_block_bwd(a, d->dtype, 0, ps_stream);
             if (e != hipSuccess) return hip_fail(e, "block backward launch");
-            st = timer.end(caller, ti, 0);
+            st = timer.end(ps_stream, ti, 0);
             if (st != RA_OK) return st;
+        }
+        if (n_streams > 1) {
+            for (int i = 0; i < n_streams; ++i) {
+                RA_HIP(hipEventRecord(ds.bwd_events[1 + i], ds.compute[i]));
+                RA_HIP(hipStreamWaitEvent(caller, ds.bwd_events[1 + i], 0));
+            }
         }
     }
     if (d->stats) {
@@ -936,6 +959,7 @@ void ra_release(void) {
         for (auto s : kv.second.copy) (void)hipStreamDestroy(s);
         for (auto e : kv.second.sync_events) (void)hipEventDestroy(e);
         for (auto e : kv.second.timing_events) (void)hipEventDestroy(e);
+        for (auto e : kv.second.bwd_events) (void)hipEventDestroy(e);
     }
     g_devices.clear();
     (void)hipSetDevice(cur);

@@ -211,6 +211,28 @@ def test_ring_backward_matches_oracle(lay, causal, dtype, D, N, S):
         gh.grad_close(gh.to_host_f64(got), ref, tol, name, extra=ex)
 
 
+@pytest.mark.parametrize("lay", ["contiguous", "striped"])
+def test_ring_backward_streams_are_bit_identical_to_one_stream(lay):
+    """The positions of a lockstep step run on several library streams, joined
+    after every step, so every dK / dV block still accumulates its shares in
+    step order: the gradients equal the one-stream run bit for bit."""
+    gh.say("ra_ring_backward streams", lay)
+    S, N, Hq, Hkv, D = 4096, 4, 4, 2, 128
+    qn, kn, vn = gh.qkv_global(1, Hq, Hkv, S, D, "bf16", seed=43)
+    gn = ra_inputs.normal((1, Hq, S, D), 3, seed=43)
+    qs, ks, vs, gs = (gh.shards_on_device(x, N, lay, "bf16") for x in (qn, kn, vn, gn))
+    o, lse, _ = gh.run_ring(qs, ks, vs, N, 0, lay, True)
+    outs = []
+    for n_streams in (1, 0, 3):
+        grads = [torch.full(t.shape, float("nan"), device="cuda") for t in (qs, ks, ks)]
+        ra.ra_ring_backward(qs, ks, vs, o, gs, lse, *grads, n_pos=N, layout=lay, causal=True, n_streams=n_streams)
+        torch.cuda.synchronize()
+        outs.append(grads)
+    for other in outs[1:]:
+        for a_, b_ in zip(outs[0], other):
+            assert torch.equal(a_, b_)
+
+
 def test_mfma_backward_runs_and_differs_from_vector_path():
     """bf16 head_dim 128 takes the MFMA kernels (P and dS rounded to bf16 for the
     products); the vector-ALU path keeps them in fp32.  Both match the oracle,
