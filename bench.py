@@ -11,9 +11,12 @@ counter-based generator and are resident in HBM before timing starts.
 Printed: one JSON line.  `value` is attention TFLOP/s counting only unmasked
 (query, key) pairs (4 * head_dim FLOPs per pair per query head), over the timed
 steps.  `roofline` describes the block-attention kernel (achieved FLOP rate from
-HIP events on its own stream vs the bf16 dense MFMA peak); `merge` the
-log-sum-exp merge kernel's algorithmic HBM rate; `cpu_baseline` times the CPU
-fp64 oracle on a bounded sample of the same workload.
+HIP events on its own stream vs the bf16 dense MFMA peak), with the gfx clock
+sampled while it ran and the fraction of the MFMA rate at that clock; `merge`
+the log-sum-exp merge kernel's algorithmic HBM rate; `cpu_baseline` times the
+CPU fp64 oracle on a bounded sample of the same workload.  With the default
+workload (the Llama-3-8B-shaped 1M-token share) `companion` holds the same
+figures for the causal 256K-token striped share, measured in the same run.
 """
 from __future__ import annotations
 
@@ -57,7 +60,8 @@ def log(*a):
 def traffic_from_profile(kernel_src, workload, record="block_attn_traffic.json"):
     """HBM bytes per block-kernel launch (or block pair, for the backward) from
     committed rocprofv3 counters, if they were taken on the current kernel
-    source and on this workload (else None)."""
+    source and on this workload (else None).  The record holds one entry per
+    workload (``workloads``: name -> {kernel_sha256, bytes_per_launch, ...})."""
     path = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(path):
         return None
@@ -65,9 +69,10 @@ def traffic_from_profile(kernel_src, workload, record="block_attn_traffic.json")
         rec = json.load(f)
     with open(kernel_src, "rb") as f:
         digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_sha256") != digest or rec.get("workload") != workload:
+    entry = rec.get("workloads", {}).get(workload)
+    if not entry or entry.get("kernel_sha256") != digest:
         return None
-    return rec.get("bytes_per_launch")
+    return entry.get("bytes_per_launch")
 
 
 def _openmp():
@@ -169,12 +174,16 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
     elapsed = time.perf_counter() - t_start
     step_ms = [e0.elapsed_time(e1) for e0, e1 in marks]
     ms_per_step = elapsed / args.steps * 1e3
-    # launch timing (HIP events around every block pair) in 3 more steps
+    # launch timing (HIP events around every block pair) in 3 more steps, on
+    # one stream for a whole ring (where the positions' launches overlap)
     tot = {"block_ms": 0.0, "block_launches": 0, "flops": 0.0}
     for _ in range(3):
-        st = ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, stats=True, **kw)
+        st = ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, stats=True,
+                                 n_streams=1 if n_run > 1 else 0, **kw)
         for key in tot:
             tot[key] += st[key]
+    clock = sustained_clock(lambda _s: ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw),
+                            torch)
     flops_per_step = tot["flops"] / 3
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     per_launch_ms = tot["block_ms"] / max(1, tot["block_launches"])
@@ -197,7 +206,9 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                      "kernel": "dq_kernel + dkdv_kernel (one block pair)", "launches": tot["block_launches"],
                      "mean_launch_ms": round(per_launch_ms, 4),
                      "timing": "HIP events around each block pair's pair of launches, 3 steps after the "
-                               "timed ones"},
+                               "timed ones",
+                     "clock": clock,
+                     "frac_at_clock": None if clock is None else round(achieved / mfma_peak_at(clock), 4)},
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:
@@ -254,42 +265,105 @@ def ring_balance(ra, torch, q_sh, k_sh, v_sh, N, sb, causal, layout_name):
     return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="CPU time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--backward", action="store_true",
-                    help="time the ring backward (dQ, dK, dV) instead of the forward")
-    ap.add_argument("--separate-merge", action="store_true",
-                    help="fold each block's partial with a separate merge launch instead of in the block kernel")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture one step in a HIP graph and time its replays (launch overhead removed)")
-    ap.add_argument("--kv-splits", type=int, default=0,
-                    help="key ranges per block launch (0: the library's automatic choice, 1: none)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the ring positions are virtual positions on a single "
-              "MI355X; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+class ClockSampler:
+    """Samples the GPU's gfx clock (mean over its XCDs) in a background thread
+    while a timed region runs, so that each rate is reported beside the clock
+    it ran at (the chip holds well under its 2.4 GHz peak clock under a full
+    MFMA load, and its XCDs differ).  Reads the GPU metrics through the amdsmi
+    library in this process (no helper program is started); without amdsmi
+    the summary is None."""
 
-    import torch
+    def __init__(self, gpu=0, period_s=0.05):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.per_xcd = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._threading = threading
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._handle = amdsmi.amdsmi_get_processor_handles()[gpu]
+        except Exception:  # no library, no permission: no clock figures
+            self._handle = None
 
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = m.get("current_gfxclks")
+        if isinstance(clks, (list, tuple)):
+            vals = [float(x) for x in clks if isinstance(x, (int, float)) and 0 < x < 10000]
+            if vals:
+                return vals
+        c = m.get("current_gfxclk")
+        return [float(c)] if isinstance(c, (int, float)) and 0 < c < 10000 else []
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                mhz = self._read()
+                if mhz and min(mhz) > 500:  # skip samples taken while the GPU idled
+                    self.samples.append(sum(mhz) / len(mhz))
+                    self.per_xcd.append(mhz)
+            except Exception:  # a failed read is just a missing sample
+                pass
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self._handle is not None:
+            self._thread = self._threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join(timeout=15)
+
+    def summary(self, skip_frac=0.0):
+        """Mean clock over the samples, the first skip_frac of them dropped (the
+        clock settles during the first part of a sustained load)."""
+        n0 = int(len(self.samples) * skip_frac)
+        s, x = self.samples[n0:], self.per_xcd[n0:]
+        if not s:
+            return None
+        widths = {len(r) for r in x}
+        xcd = np.mean(np.array(x), axis=0).tolist() if len(widths) == 1 else None
+        return {"mean_mhz": round(float(np.mean(s)), 1), "min_mhz": round(float(np.min(s)), 1),
+                "max_mhz": round(float(np.max(s)), 1), "samples": len(s),
+                "per_xcd_mean_mhz": None if xcd is None else [round(float(v), 1) for v in xcd],
+                "source": "amdsmi gpu metrics (current gfx clock of each XCD)"}
+
+
+def sustained_clock(run_step, torch, seconds=2.5):
+    """The gfx clock under this workload's sustained load: the step repeated
+    back to back for about `seconds` while the clock is sampled (first third
+    of the samples dropped)."""
+    with ClockSampler() as clk:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            run_step(False)
+            torch.cuda.synchronize()
+    return clk.summary(skip_frac=1 / 3)
+
+
+def mfma_peak_at(clock):
+    """Dense bf16 MFMA rate of the whole chip at a clock (256 CUs x 4096 FLOP/clk)."""
+    return None if clock is None else 256 * 4096 * clock["mean_mhz"] * 1e6 / 1e12
+
+
+def run_forward(args, name, ra, torch, dev, cpu_seconds, quiet=False):
+    """Forward measurement of one workload: the timed steps, the block kernel's
+    roofline, the merge rate, ring balance and the CPU baseline.  Returns the
+    JSON record (without printing it)."""
     import ra_inputs
-    import ring_attention_step_amd as ra
 
-    cfg = WORKLOADS[args.workload]
+    cfg = WORKLOADS[name]
     B, Hq, Hkv, S, D, N, lay = (cfg[k] for k in ("B", "Hq", "Hkv", "S", "D", "N", "layout"))
     sb = S // N
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    ra.load_library()
-
-    log(f"workload {args.workload}: generating inputs")
+    log(f"workload {name}: generating inputs")
     t0 = time.perf_counter()
     k_np = ra_inputs.normal((B, Hkv, S, D), ra_inputs.STREAM_K, seed=args.seed, dtype="bf16")
     v_np = ra_inputs.normal((B, Hkv, S, D), ra_inputs.STREAM_V, seed=args.seed, dtype="bf16")
@@ -345,7 +419,7 @@ def main():
 
     if args.backward:
         run_backward(args, cfg, ra, torch, step, q_sh, k_sh, v_sh, o_sh, lse, first, n_run, dev, k_np, v_np, q_rows)
-        return
+        return None
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -412,13 +486,19 @@ def main():
     per_launch_ms = rt["block_ms"] / max(1, rt["block_launches"])
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"),
-                                   args.workload)
+                                   name)
+    log("clock under sustained load")
+    clock = sustained_clock(run_step, torch)
+    at_clock = mfma_peak_at(clock)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "block_mfma_kernel<128>" if D == 128 else "block_mfma_kernel<64>",
                 "launches": rt["block_launches"], "mean_launch_ms": round(per_launch_ms, 4),
                 "timing": "HIP events around each launch on its stream, 3 steps after the timed ones" +
-                          (" (on one stream)" if n_run > 1 else "")}
+                          (" (on one stream)" if n_run > 1 else ""),
+                "clock": clock,  # gfx clock while the step repeats back to back (amdsmi)
+                "peak_at_clock": None if at_clock is None else round(at_clock, 1),
+                "frac_at_clock": None if at_clock is None else round(achieved / at_clock, 4)}
 
     # merge kernel: algorithmic bytes per step.  A state (fp32 O, m, l) is
     # 4 D + 8 bytes a row, a finalised row (bf16 output, log-sum-exp) 2 D + 4.
@@ -457,22 +537,22 @@ def main():
         balance = ring_balance(ra, torch, q_sh, k_sh, v_sh, N, sb, cfg["causal"], lay)
 
     cpu = None
-    if args.cpu_seconds > 0:
-        log(f"cpu baseline: oracle for about {args.cpu_seconds:.0f} s on all cores, then a third of that on one")
-        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds)
-        one = cpu_baseline(cfg, k_np, v_np, q_rows, args.cpu_seconds / 3, threads=1)
+    if cpu_seconds > 0:
+        log(f"cpu baseline: oracle for about {cpu_seconds:.0f} s on all cores, then a third of that on one")
+        cpu = cpu_baseline(cfg, k_np, v_np, q_rows, cpu_seconds)
+        one = cpu_baseline(cfg, k_np, v_np, q_rows, cpu_seconds / 3, threads=1)
         cpu["one_core"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"]}
         # the oracle over one whole step of this workload, at the measured rate (extrapolated)
         cpu["extrapolated_step_s"] = round(flops_per_step / (cpu["value"] * 1e12), 1)
 
-    line = {
+    return {
         "metric": "ring-attention fwd TFLOP/s (causal-adjusted) + % of MI355X bf16 MFMA peak",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_median": round(float(np.median(step_ms)), 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "config": {"workload": args.workload, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
+        "config": {"workload": name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
                    "head_dim": D, "ring_positions": N, "layout": lay, "causal": cfg["causal"],
                    "positions_run": n_run, "first_position": first,
                    "merge_schedule": "separate" if args.separate_merge else "fused", "kv_splits": splits,
@@ -481,6 +561,55 @@ def main():
         "roofline": roofline, "merge": merge, "cpu_baseline": cpu,
         "ring_balance": balance,
     }
+
+
+# the second causal striped workload measured beside the default one
+COMPANION = "causal-256k-striped-share"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the ring backward (dQ, dK, dV) instead of the forward")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="fold each block's partial with a separate merge launch instead of in the block kernel")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (launch overhead removed)")
+    ap.add_argument("--kv-splits", type=int, default=0,
+                    help="key ranges per block launch (0: the library's automatic choice, 1: none)")
+    ap.add_argument("--no-companion", action="store_true",
+                    help=f"with the default workload, skip the {COMPANION} measurement reported beside it")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ring positions are virtual positions on a single "
+              "MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ring_attention_step_amd as ra
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    ra.load_library()
+
+    line = run_forward(args, args.workload, ra, torch, dev, args.cpu_seconds)
+    if line is None:  # the backward printed its own line
+        return
+    if args.workload == DEFAULT and not args.no_companion and not args.backward:
+        # the other causal striped workload, whose block kernel carries the same
+        # 50%-of-peak target: measured in the same run, on the same GPU
+        torch.cuda.empty_cache()
+        comp = run_forward(args, COMPANION, ra, torch, dev, 0)
+        line["companion"] = {k: comp[k] for k in ("config", "value", "ms_per_step", "ms_per_step_median",
+                                                  "pct_of_bf16_peak", "roofline", "merge")}
     print(json.dumps(line), flush=True)
 
 
