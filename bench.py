@@ -159,8 +159,9 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
     dv = torch.empty_like(dk)
     kw = dict(n_pos=N, first_pos=first, layout=lay, causal=cfg["causal"])
     log(f"backward warmup {args.warmup}")
+    timed_kw = dict(kw, n_streams=args.n_streams)
     for _ in range(args.warmup):
-        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw)
+        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **timed_kw)
     torch.cuda.synchronize()
     log(f"backward timing {args.steps} steps")
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -168,7 +169,7 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
     t_start = time.perf_counter()
     for e0, e1 in marks:
         e0.record()
-        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw)
+        ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **timed_kw)
         e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
@@ -182,8 +183,8 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
                                  n_streams=1 if n_run > 1 else 0, **kw)
         for key in tot:
             tot[key] += st[key]
-    clock = sustained_clock(lambda _s: ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv, **kw),
-                            torch)
+    clock = sustained_clock(lambda _s: ra.ra_ring_backward(q_sh, k_sh, v_sh, o_sh, dout, lse, dq, dk, dv,
+                                                           **timed_kw), torch)
     flops_per_step = tot["flops"] / 3
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     per_launch_ms = tot["block_ms"] / max(1, tot["block_launches"])
@@ -194,7 +195,8 @@ def run_backward(args, cfg, ra, torch, fwd_step, q_sh, k_sh, v_sh, o_sh, lse, fi
         "ms_per_step": round(ms_per_step, 4), "ms_per_step_median": round(float(np.median(step_ms)), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-        "config": {"workload": args.workload, "pass": "backward", "batch": B, "q_heads": Hq,
+        "config": {"workload": args.workload, "pass": "backward", "n_streams": args.n_streams, "batch": B,
+                   "q_heads": Hq,
                    "kv_heads": cfg["Hkv"], "seq_len": S, "head_dim": D, "ring_positions": N, "layout": lay,
                    "causal": cfg["causal"], "positions_run": n_run, "first_position": first,
                    "unmasked_flops_per_step": flops_per_step},
@@ -405,7 +407,7 @@ def run_forward(args, name, ra, torch, dev, cpu_seconds, quiet=False):
     workspace = torch.empty(ra.ra_ring_workspace_size(desc), dtype=torch.uint8, device=dev)
     kv_splits = args.kv_splits
 
-    def step(stats, n_streams=0):
+    def step(stats, n_streams=args.n_streams):
         ra.ra_stripe_permute(k_g, k_sh, layout=lay, inverse=False, n_pos=N)
         ra.ra_stripe_permute(v_g, v_sh, layout=lay, inverse=False, n_pos=N)
         if q_g is not None:
@@ -584,6 +586,8 @@ def main():
                     help="capture one step in a HIP graph and time its replays (launch overhead removed)")
     ap.add_argument("--kv-splits", type=int, default=0,
                     help="key ranges per block launch (0: the library's automatic choice, 1: none)")
+    ap.add_argument("--n-streams", type=int, default=0,
+                    help="library streams a whole ring's positions run on (0: the library's choice)")
     ap.add_argument("--no-companion", action="store_true",
                     help=f"with the default workload, skip the {COMPANION} measurement reported beside it")
     args = ap.parse_args()

@@ -161,7 +161,9 @@ __device__ inline int xcd_remap(int w, int n) {
 // the next launch (no workgroup of this launch reads them any more).
 // Two waves per SIMD (<= 256 registers): one wave's MFMAs overlap the other's
 // softmax arithmetic.
-template <int D, int WAVES>
+// FULL: every key range the launch visits is a whole number of kNk-key tiles
+// (no ragged last tile), so the in-stream tile copies need no row clamp.
+template <int D, int WAVES, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_mfma_kernel(
     const BlockArgs a) {
     constexpr int kMq = 32 * WAVES;
@@ -308,9 +310,20 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
         static_assert(INSTR % (WAVES / 2) == 0, "tile copy must split evenly over a wave group");
         const int wslot = wave % (WAVES / 2);
         const int crow0 = wslot * PER_G * RPI + lane / CPR;
-        uint32_t cc16[PER_G];
+        // The chunk a lane fetches for instruction i depends on i only through
+        // swz(crow0 + RPI i), which repeats with period 4 in i (RPI is a
+        // multiple of 4), so FULL copies use one of four per-lane byte offsets
+        // (row crow0's) and advance the rows through the wave-uniform base
+        // address: no vector arithmetic between the MFMAs.  Otherwise each
+        // instruction clamps its row to the block's last one.
+        constexpr int NOFF = FULL ? (PER_G < 4 ? PER_G : 4) : PER_G;
+        uint32_t cc16[NOFF];
 #pragma unroll
-        for (int i = 0; i < PER_G; ++i) cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
+        for (int i = 0; i < NOFF; ++i) {
+            cc16[i] = static_cast<uint32_t>(((lane % CPR) ^ swz<D>(crow0 + RPI * i)) * 16);
+            // the tensor this wave's group copies: K for waves 0 .. WAVES/2 - 1, V for the rest
+            if (FULL) cc16[i] += static_cast<uint32_t>(crow0 * (wave < WAVES / 2 ? ks2 : vs2) * 2);
+        }
 
         // per-lane LDS byte offsets of the operand reads
         const lds_char* lds = RA_LDS_PTR(char, smem);
@@ -509,8 +522,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2
             mfma_stream.template operator()<PV, QK, PRE>(t - 1, t, [&](int n) __attribute__((always_inline)) {
                 if (QK && n % kStep == 0 && n / kStep < PER_G) {
                     const int i = n / kStep;
-                    const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
-                    lds_dma16(src, o, dst + i * 1024);
+                    if constexpr (FULL) {
+                        lds_dma16(src + static_cast<int64_t>(RPI * i) * stride, cc16[i % NOFF], dst + i * 1024);
+                    } else {
+                        const uint32_t o = static_cast<uint32_t>(min(crow0 + RPI * i, last)) * stride2 + cc16[i];
+                        lds_dma16(src, o, dst + i * 1024);
+                    }
                 }
             });
             if (RA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -677,12 +694,17 @@ hipError_t launch_block_mfma(const BlockArgs& a, hipStream_t s) {
     int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B * a.n_splits;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;  // tile ids are 32-bit
     if (a.queue) blocks = std::min<int64_t>(blocks, compute_units());  // one looping workgroup per CU
-    if (a.D == 128)
-        hipLaunchKernelGGL((block_mfma_kernel<128, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
-                           0, s, a);
-    else
-        hipLaunchKernelGGL((block_mfma_kernel<64, kWaves>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kWaves),
-                           0, s, a);
+    // whole tiles only (every key range a multiple of kNk keys): copies without row clamps
+    // (key splits cut at tile boundaries, so their ranges are whole tiles too)
+    const bool full = a.kv_len % kNk == 0;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
+    if (a.D == 128) {
+        if (full) hipLaunchKernelGGL((block_mfma_kernel<128, kWaves, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((block_mfma_kernel<128, kWaves, false>), grid, block, 0, s, a);
+    } else {
+        if (full) hipLaunchKernelGGL((block_mfma_kernel<64, kWaves, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((block_mfma_kernel<64, kWaves, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
