@@ -195,7 +195,14 @@ typedef struct ra_ring_desc {
                                 (double buffer) by device-to-device copies on
                                 a copy stream, ordered by HIP events, as a ring
                                 transfer would be                              */
-    int32_t n_streams;  /* compute streams; 0 = min(n_run, 8)                     */
+    int32_t n_streams;  /* compute streams; 0 = min(n_run, 8).  A single position
+                           (n_run = 1) whose block launches hold at least twice
+                           as many query tiles as the GPU has compute units
+                           (bf16, head_dim 64 or 128, fused schedule, no
+                           emulate_copy) runs its computed steps alternately on
+                           two running states on two streams when n_streams is
+                           0 or >= 2, and the final merge pass folds the second
+                           into the first; n_streams = 1 keeps one state      */
     int32_t separate_merge; /* 0: each step after a position's first merges its
                                partial into the running state inside the block
                                kernel (RA_BLOCK_ACCUMULATE) and one finalising

@@ -246,6 +246,7 @@ struct RingGeometry {
     int64_t q_elems;    // B * Hq * Sb * D   (one position's query shard / output)
     int64_t kv_elems;   // B * Hkv * Sb * D  (one key or value shard)
     int32_t n_streams;
+    int32_t n_chains;               // accumulation chains of a single position (1 or 2)
     int32_t n_splits, split_tiles;  // key splits of every block launch (1: none)
     int32_t n_part;                 // partials per stream (0, 1 or n_splits)
     size_t acc_o, acc_ml, part_o, part_ml, slot;  // bytes, each 256-aligned
@@ -311,14 +312,31 @@ RingGeometry geometry(const ra_ring_desc* d) {
             g.n_splits = static_cast<int32_t>((tiles + g.split_tiles - 1) / g.split_tiles);  // no empty range
         }
     }
+    // Accumulation chains.  One position's fused steps run one after another
+    // on one stream, each launch folding into the running state, so every
+    // launch's start (claims, Q loads, first tile copies) and end (compute
+    // units running out of tiles) are paid in full.  When a single position
+    // runs large launches (the work queues' threshold), its computed steps
+    // alternate between two running states on two streams instead: the
+    // launches of one chain overlap the start and end of the other's, and the
+    // final merge pass folds the second state into the first and normalises.
+    g.n_chains = 1;
+    if (d->n_run == 1 && !d->separate_merge && g.n_splits == 1 && !d->emulate_copy && d->n_pos >= 2 &&
+        (d->n_streams == 0 || d->n_streams >= 2) && d->dtype == RA_BF16 && (d->head_dim == 64 || d->head_dim == 128)) {
+        const int64_t launch_tiles =
+            (Sb + ra::mfma_query_tile() - 1) / ra::mfma_query_tile() * d->q_heads * d->batch;
+        if (launch_tiles >= 2 * static_cast<int64_t>(ra::compute_units())) g.n_chains = 2;
+    }
+    if (g.n_chains > 1) g.n_streams = g.n_chains;
     g.n_part = d->separate_merge ? 1 : (g.n_splits > 1 ? g.n_splits : 0);
     g.part_o = g.n_part ? g.acc_o : 0;
     g.part_ml = g.n_part ? g.acc_ml : 0;
     g.slot = d->emulate_copy ? round_up(static_cast<size_t>(g.kv_elems) * elem_size(d->dtype), 256) : 0;
     g.queue = round_up(ra::kQueueWords * sizeof(uint32_t), 256);
-    // per run position: acc o, m, l (+ 2 slots x {K, V});  per stream: n_part
-    // partials o, m, l and the tile-queue counters of its block launches
-    g.total = static_cast<size_t>(d->n_run) * (g.acc_o + 2 * g.acc_ml + 4 * g.slot) +
+    // per run position: n_chains running states o, m, l (+ 2 slots x {K, V});
+    // per stream: n_part partials o, m, l and the tile-queue counters of its
+    // block launches
+    g.total = static_cast<size_t>(d->n_run) * (g.n_chains * (g.acc_o + 2 * g.acc_ml) + 4 * g.slot) +
               static_cast<size_t>(g.n_streams) * (g.n_part * (g.part_o + 2 * g.part_ml) + g.queue);
     return g;
 }
@@ -429,17 +447,19 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
     // carve the workspace
     char* ws = static_cast<char*>(workspace);
     struct PosBufs {
-        float *o, *m, *l;
-        char* slot[2][2];  // [parity][K=0 / V=1]
+        float *o[2], *m[2], *l[2];  // running state of each accumulation chain
+        char* slot[2][2];           // [parity][K=0 / V=1]
     };
     std::vector<PosBufs> pos(d->n_run);
     for (int p = 0; p < d->n_run; ++p) {
-        pos[p].o = reinterpret_cast<float*>(ws);
-        ws += g.acc_o;
-        pos[p].m = reinterpret_cast<float*>(ws);
-        ws += g.acc_ml;
-        pos[p].l = reinterpret_cast<float*>(ws);
-        ws += g.acc_ml;
+        for (int c = 0; c < g.n_chains; ++c) {
+            pos[p].o[c] = reinterpret_cast<float*>(ws);
+            ws += g.acc_o;
+            pos[p].m[c] = reinterpret_cast<float*>(ws);
+            ws += g.acc_ml;
+            pos[p].l[c] = reinterpret_cast<float*>(ws);
+            ws += g.acc_ml;
+        }
         for (int par = 0; par < 2; ++par)
             for (int kv = 0; kv < 2; ++kv) {
                 pos[p].slot[par][kv] = d->emulate_copy ? ws : nullptr;
@@ -490,8 +510,9 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
     if (own_streams) {
         st = ensure_streams(ds, g.n_streams);
         if (st != RA_OK) return st;
-        // sync events: fork, per-stream join, per (position, parity) copied / used
-        const size_t n_sync = 1 + g.n_streams + 4 * static_cast<size_t>(d->n_run);
+        // sync events: fork, per-stream join, per (position, parity) copied /
+        // used, and the join of a second accumulation chain
+        const size_t n_sync = 2 + g.n_streams + 4 * static_cast<size_t>(d->n_run);
         st = ensure_events(ds.sync_events, n_sync, hipEventDisableTiming);
         if (st != RA_OK) return st;
     }
@@ -499,6 +520,7 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
     auto ev_join = [&](int s) { return ds.sync_events[1 + s]; };
     auto ev_copied = [&](int p, int par) { return ds.sync_events[1 + g.n_streams + 4 * p + par]; };
     auto ev_used = [&](int p, int par) { return ds.sync_events[1 + g.n_streams + 4 * p + 2 + par]; };
+    auto ev_chain = [&]() { return ds.sync_events[1 + g.n_streams + 4 * static_cast<size_t>(d->n_run)]; };
     // the stream position p's work (and the queue counters of stream slot s) run on
     auto compute_stream = [&](int s) { return own_streams ? ds.compute[s] : caller; };
 
@@ -563,7 +585,9 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
     for (int32_t s = 0; s < N; ++s) {
         for (int p = 0; p < d->n_run; ++p) {
             const RingPlanStep& ps = plan[p][s];
-            const int sid = p % g.n_streams;
+            // the chain (and stream) of this position's next computed step
+            const int chain = done[p] % g.n_chains;
+            const int sid = g.n_chains > 1 ? chain : p % g.n_streams;
             const hipStream_t cs = compute_stream(sid);
             const int par = s & 1;
             const void* kp = kb + static_cast<size_t>(ps.block) * kv_bytes;
@@ -574,7 +598,7 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
             }
             if (!ps.skip) {
                 if (d->emulate_copy) RA_HIP(hipStreamWaitEvent(cs, ev_copied(p, par), 0));
-                const bool first = done[p] == 0;
+                const bool first = done[p] < g.n_chains;  // the chain's first step: it writes its state
                 const bool last = done[p] + 1 == n_computed[p];
                 const bool fused = !d->separate_merge;
                 ra::BlockArgs a{};
@@ -582,9 +606,9 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
                 a.k = kp;
                 a.v = vp;
                 const bool into_acc = first || fused;
-                a.o = into_acc ? pos[p].o : part[sid].o;
-                a.m = into_acc ? pos[p].m : part[sid].m;
-                a.l = into_acc ? pos[p].l : part[sid].l;
+                a.o = into_acc ? pos[p].o[chain] : part[sid].o;
+                a.m = into_acc ? pos[p].m[chain] : part[sid].m;
+                a.l = into_acc ? pos[p].l[chain] : part[sid].l;
                 a.accumulate = (fused && !first) ? 1 : 0;
                 a.B = d->batch;
                 a.Hq = d->q_heads;
@@ -629,13 +653,23 @@ ra_status ring_forward_run(const ra_ring_desc* d, const void* q, const void* k, 
                     ra::MergeArgs ma{};
                     ma.rows = g.rows;
                     ma.D = D;
-                    ma.o_acc = pos[p].o;
-                    ma.m_acc = pos[p].m;
-                    ma.l_acc = pos[p].l;
+                    ma.o_acc = pos[p].o[chain];
+                    ma.m_acc = pos[p].m[chain];
+                    ma.l_acc = pos[p].l[chain];
                     if ((!first && !fused) || split) {
                         ma.o_p = part[sid].o;
                         ma.m_p = part[sid].m;
                         ma.l_p = part[sid].l;
+                    }
+                    if (last && g.n_chains > 1 && n_computed[p] > 1) {
+                        // the other chain's state is the partial folded in by
+                        // the finalising pass, once that chain's stream is done
+                        const int other = 1 - chain;
+                        RA_HIP(hipEventRecord(ev_chain(), compute_stream(other)));
+                        RA_HIP(hipStreamWaitEvent(cs, ev_chain(), 0));
+                        ma.o_p = pos[p].o[other];
+                        ma.m_p = pos[p].m[other];
+                        ma.l_p = pos[p].l[other];
                     }
                     if (split) {
                         ma.n_parts = g.n_splits;

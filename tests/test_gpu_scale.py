@@ -38,11 +38,18 @@ def test_config4_causal_striped_full_ring_and_share():
     sh, stt = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=1)
     assert len(set(zip(sh.tolist(), stt.tolist()))) == 4096
     gh.compare_rows(o, lse, qn, kn, vn, sh, stt, N, "striped", 0, True, "bf16")
-    # one position's share (the benchmarked unit) equals that position of the full ring, bitwise
+    # one position's share (the benchmarked unit) on one stream equals that
+    # position of the full ring, bitwise; the default schedule of a share
+    # (two accumulation chains) agrees to rounding and with the oracle
     gh.say("ra_ring_forward config4 share")
-    o7, lse7, st7 = gh.run_ring(qs[7:8].contiguous(), ks, vs, N, 7, "striped", True, stats=True)
+    o7, lse7, st7 = gh.run_ring(qs[7:8].contiguous(), ks, vs, N, 7, "striped", True, stats=True, n_streams=1)
     assert torch.equal(o7[0], o[7]) and torch.equal(lse7[0], lse[7])
     assert st7["flops"] == 4 * D * H * N * (S // N) * (S // N + 1) // 2
+    o7c, lse7c, _ = gh.run_ring(qs[7:8].contiguous(), ks, vs, N, 7, "striped", True)
+    assert torch.max(torch.abs(o7c.float() - o7.float())) <= 1e-2
+    assert torch.max(torch.abs(lse7c - lse7)) <= 1e-5
+    sh7, st7t = ra_inputs.sample_rows(S, N, 4096, heads=H, seed=2, share=7, layout="striped")
+    gh.compare_rows(o7c, lse7c, qn, kn, vn, sh7, st7t, N, "striped", 7, True, "bf16")
 
 
 @pytest.mark.timeout(1200)
