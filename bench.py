@@ -463,17 +463,19 @@ def run_forward(args, name, ra, torch, dev, cpu_seconds, quiet=False):
     ms_per_step = elapsed / args.steps * 1e3
     value = flops_per_step / (ms_per_step * 1e-3) / 1e12
     log(f"{ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+    log("clock under sustained load")
+    clock = sustained_clock(run_step, torch)
 
     # block-attention kernel roofline: algorithmic FLOPs per launch / mean launch
     # time, from HIP events around every launch in 3 steps after the timed
-    # region.  A full ring runs its positions on several streams, where launches
-    # overlap and event spans overstate each one; its launches are then timed
-    # on one stream, with the key ranges of the timed steps.
+    # region.  The timed schedule may run launches on several streams (the
+    # positions of a whole ring, the two accumulation chains of a share), where
+    # launches overlap and event spans overstate each one; the launches are
+    # therefore timed on one stream, with the key ranges of the timed steps.
     n_stat = 3
     rt = {"block_ms": 0.0, "block_launches": 0, "merge_ms": 0.0, "merge_launches": 0, "flops": 0.0}
-    stat_streams = 0
+    stat_streams = 1
     if n_run > 1:
-        stat_streams = 1
         kv_splits = splits  # whatever one stream alone would choose
         if splits > 1:
             workspace = torch.empty(ra.ra_ring_workspace_size(ra.ring_desc(
@@ -489,8 +491,6 @@ def run_forward(args, name, ra, torch, dev, cpu_seconds, quiet=False):
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
     traffic = traffic_from_profile(os.path.join(ROOT, "ring_attention_step_amd", "csrc", "block_attn_mfma.hip"),
                                    name)
-    log("clock under sustained load")
-    clock = sustained_clock(run_step, torch)
     at_clock = mfma_peak_at(clock)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
