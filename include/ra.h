@@ -362,9 +362,11 @@ ra_status ra_ring_bwd_workspace_size(const ra_ring_desc* desc, size_t* bytes);
  * j = (i - visit_order[s]) mod n_pos (distinct across positions) and adds its
  * share into its own dq and into the block's dk, dv.  Fully masked pairs are
  * skipped.  The positions of one step write disjoint outputs and run on
- * n_streams library streams (0: min(n_run, 8); position p on stream p mod
- * n_streams), forked from `stream` before each step and joined back to it
- * after; emulate_copy and separate_merge are ignored.  With desc->stats,
+ * n_streams library streams (position p on stream p mod n_streams), forked
+ * from `stream` before each step and joined back to it after.  n_streams = 0
+ * picks one stream (the caller's) when each launch's dQ and dK/dV kernels
+ * both hold at least one workgroup per compute unit (bf16, head_dim 64 or
+ * 128), else min(n_run, 8).  emulate_copy and separate_merge are ignored.  With desc->stats,
  * backward launches are timed (block_ms, block_launches; spans of launches on
  * different streams may overlap) and flops counts the five products.
  *

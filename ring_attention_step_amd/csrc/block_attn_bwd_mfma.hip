@@ -36,6 +36,7 @@
 // vector work interleave as they fall; a wave raises its priority while it
 // issues its S and dP chains, so that those win the SIMD's issue over the
 // other wave's vector work.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <type_traits>
@@ -639,10 +640,21 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     return true;
 }
 
+namespace {
+int64_t dq_workgroups(const BwdArgs& a) {
+    return static_cast<int64_t>((a.q_len + 32 * kDqWaves - 1) / (32 * kDqWaves)) * a.Hq * a.B;
+}
+int64_t dkdv_workgroups(const BwdArgs& a) {
+    return static_cast<int64_t>((a.kv_len + 32 * kKvWaves - 1) / (32 * kKvWaves)) * a.Hkv * a.B;
+}
+}  // namespace
+
+int64_t bwd_mfma_min_workgroups(const BwdArgs& a) { return std::min(dq_workgroups(a), dkdv_workgroups(a)); }
+
 hipError_t launch_block_bwd_mfma(const BwdArgs& a, hipStream_t s) {
     if (a.q_len == 0 || a.kv_len == 0) return hipSuccess;
-    const int64_t qb = static_cast<int64_t>((a.q_len + 32 * kDqWaves - 1) / (32 * kDqWaves)) * a.Hq * a.B;
-    const int64_t kb = static_cast<int64_t>((a.kv_len + 32 * kKvWaves - 1) / (32 * kKvWaves)) * a.Hkv * a.B;
+    const int64_t qb = dq_workgroups(a);
+    const int64_t kb = dkdv_workgroups(a);
     if (a.D == 128) {
         hipLaunchKernelGGL(dq_kernel<128>, dim3(static_cast<unsigned>(qb)), dim3(64 * kDqWaves), 0, s, a);
         hipLaunchKernelGGL(dkdv_kernel<128>, dim3(static_cast<unsigned>(kb)), dim3(64 * kKvWaves), 0, s, a);

@@ -896,11 +896,22 @@ ra_status ra_ring_backward(const ra_ring_desc* d, const void* q, const void* k, 
     DeviceState& ds = g_devices[dev];
     Timer timer;
     if (d->stats) timer.pool = &ds.timing_events;
-    // the positions of one step write disjoint dq and dk / dv, so they run on
-    // n_streams library streams, forked from the caller's stream before every
-    // step and joined back after it (the next step hands every block to
-    // another position)
-    const int n_streams = d->n_streams > 0 ? std::min(d->n_streams, d->n_run) : std::min(d->n_run, 8);
+    // the positions of one step write disjoint dq and dk / dv, so they may run
+    // on n_streams library streams, forked from the caller's stream before
+    // every step and joined back after it (the next step hands every block to
+    // another position).  Automatic: one stream when each of a launch's two
+    // kernels already holds a workgroup per compute unit (concurrent launches
+    // then only contend for the same units: measured slower), else
+    // min(n_run, 8).
+    int n_streams = d->n_streams > 0 ? std::min(d->n_streams, d->n_run) : std::min(d->n_run, 8);
+    if (d->n_streams == 0 && d->dtype == RA_BF16 && (D == 64 || D == 128)) {
+        ra::BwdArgs g{};
+        g.B = d->batch;
+        g.Hq = d->q_heads;
+        g.Hkv = d->kv_heads;
+        g.q_len = g.kv_len = static_cast<int32_t>(Sb);
+        if (ra::bwd_mfma_min_workgroups(g) >= ra::compute_units()) n_streams = 1;
+    }
     if (n_streams > 1) {
         st = ensure_streams(ds, n_streams);
         if (st != RA_OK) return st;

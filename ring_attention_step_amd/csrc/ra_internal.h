@@ -83,6 +83,8 @@ hipError_t launch_block_bwd_simt(const BwdArgs& a, int dtype, hipStream_t s);
 // bf16 MFMA backward (gfx950): D in {64, 128}; 16-byte aligned rows and outputs.
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype);
 hipError_t launch_block_bwd_mfma(const BwdArgs& a, hipStream_t s);
+// workgroups of the smaller of the two MFMA backward launches (dQ, dK/dV)
+int64_t bwd_mfma_min_workgroups(const BwdArgs& a);
 // Kernel selection for the backward (MFMA where eligible unless force_simt).
 hipError_t launch_block_bwd(const BwdArgs& a, int dtype, int force_simt, hipStream_t s);
 // x[0 .. n) = 0 (fp32), a fill kernel rather than a memset node.

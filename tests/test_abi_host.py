@@ -165,9 +165,19 @@ def test_ring_workspace_and_validation(lib):
     d = _ring_desc()
     assert lib.ra_ring_workspace_size(ctypes.byref(d), ctypes.byref(n)) == B.RA_OK
     rows = 32 * 32768
-    # fused schedule: one running state (fp32 O, m, l) per computed position,
-    # and one 256-byte block of tile-queue counters per stream (one stream here)
-    assert n.value == rows * 128 * 4 + 2 * rows * 4 + QUEUE
+    state = rows * 128 * 4 + 2 * rows * 4  # fp32 O, m, l of the 32768 queries x 32 heads
+    # a single position whose launches hold 8192 query tiles (>= 2 per compute
+    # unit) keeps two running states (accumulation chains), one 256-byte block
+    # of tile-queue counters per chain's stream
+    assert n.value == 2 * state + 2 * QUEUE
+    # n_streams = 1: one running state and one stream
+    one = _ring_desc(n_streams=1)
+    assert lib.ra_ring_workspace_size(ctypes.byref(one), ctypes.byref(n)) == B.RA_OK
+    assert n.value == state + QUEUE
+    # a single position of few query tiles (256) keeps one state with n_streams = 0
+    small = _ring_desc(q_heads=8, kv_heads=8, block_len=4096, kv_splits=1)
+    assert lib.ra_ring_workspace_size(ctypes.byref(small), ctypes.byref(n)) == B.RA_OK
+    assert n.value == (8 * 4096) * 128 * 4 + 2 * (8 * 4096) * 4 + QUEUE
     s = _ring_desc(separate_merge=1)  # plus one partial per stream
     assert lib.ra_ring_workspace_size(ctypes.byref(s), ctypes.byref(n)) == B.RA_OK
     assert n.value == 2 * (rows * 128 * 4 + 2 * rows * 4) + QUEUE
