@@ -361,6 +361,83 @@ def test_backward_256k_share_sampled_rows_and_identities():
     assert float(torch.max(torch.abs(qd - kd))) <= 2e-2 * scale
 
 
+@pytest.mark.timeout(900)
+def test_backward_gqa_1m_share_sampled_rows():
+    """The Llama-3-8B-shaped GQA share at full size (32 query heads on 8
+    key/value heads, d 128, 1M tokens striped over 32 positions, position 31's
+    share: 32768 queries against 32 blocks), elementwise against the oracle:
+    dQ on 1024 distinct sampled rows of the share (all heads); dK and dV on 256
+    sampled keys of key/value head 5, drawn from every block among the keys of
+    the last 16384 tokens -- the share rows that see them are its last 512 of
+    the head's four query heads, whose full-key-set lse and delta the oracle
+    computes, and whose shares add up in each key's gradient.  Plus, per
+    key/value head, sum_c dK_c = 0 and sum_c dV_c = the sum of dO over the
+    group's query heads and the share's rows."""
+    gh.say("ra_ring_backward gqa 1m share inputs")
+    Hq, Hkv, S, D, N, i = 32, 8, 1 << 20, 128, 32, 31
+    grp, sb = Hq // Hkv, S // N
+    kn = ra_inputs.normal((1, Hkv, S, D), 1, seed=0, dtype="bf16")
+    vn = ra_inputs.normal((1, Hkv, S, D), 2, seed=0, dtype="bf16")
+    qn = ra_inputs.normal((1, Hq, S, D), 0, seed=0, dtype="bf16", t0=i, t_stride=N, n_rows=sb)
+    gn = ra_inputs.normal((1, Hq, S, D), 3, seed=0, dtype="bf16", t0=i, t_stride=N, n_rows=sb)
+    ks, vs = (gh.shards_on_device(x, N, "striped", "bf16") for x in (kn, vn))
+    q, g = gh.to_device(qn, "bf16")[None], gh.to_device(gn, "bf16")[None]
+    gh.say("ra_ring_backward gqa 1m share")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:4], device="cuda")
+    ra.ra_ring_forward(q, ks, vs, o, lse, n_pos=N, first_pos=i, layout="striped", causal=True)
+    dq = torch.empty(q.shape, device="cuda")
+    dk = torch.empty(ks.shape, device="cuda")
+    dv = torch.empty(ks.shape, device="cuda")
+    st = ra.ra_ring_backward(q, ks, vs, o, g, lse, dq, dk, dv, n_pos=N, first_pos=i, layout="striped",
+                             causal=True, stats=True)
+    torch.cuda.synchronize()
+    assert st["block_launches"] == N and st["blocks_skipped"] == 0
+    rtol = gh.GRAD_RTOL["bf16"]
+    gh.say("ra_ring_backward gqa 1m share: dq rows")
+    sh, stt = ra_inputs.sample_rows(S, N, 1024, heads=Hq, seed=1, share=i, layout="striped")
+    assert len(set(zip(sh.tolist(), stt.tolist()))) == 1024
+    rr = (stt - i) // N
+    got = gh.to_host_f64(dq[0, 0][torch.as_tensor(sh, device="cuda"), torch.as_tensor(rr, device="cuda")])
+    want, o_ref, pk_ref = np.empty_like(got), np.empty_like(got), np.empty_like(got)
+    for h in np.unique(sh):
+        idx = np.nonzero(sh == h)[0]
+        kv = h // grp
+        r = oracle.grads(qn[0, h][rr[idx]], kn[0, kv], vn[0, kv], gn[0, h][rr[idx]], q_pos=stt[idx], causal=True,
+                         key_grads=False)
+        want[idx] = r["dq"]
+        o_ref[idx] = oracle.rows(qn[0, h][rr[idx]], kn[0, kv], vn[0, kv], q_pos=stt[idx], causal=True)["o"]
+        pk_ref[idx] = oracle.rows(qn[0, h][rr[idx]], kn[0, kv], kn[0, kv], q_pos=stt[idx], causal=True)["o"]
+    extra = gh.dq_delta_bound(o_ref, pk_ref, gn[0][sh, rr], 1.0 / np.sqrt(D))
+    gh.grad_close(got, want, rtol, "dq, 1024 sampled share rows", extra=extra)
+    gh.say("ra_ring_backward gqa 1m share: dk, dv keys")
+    kv = 5
+    rows_late = np.arange(sb - 512, sb)
+    t_late = i + N * rows_late
+    rng = np.random.Generator(np.random.PCG64(2))
+    flat = rng.choice(N * 512, size=256, replace=False)
+    jj, cc = flat // 512, sb - 512 + flat % 512
+    tok = jj + N * cc
+    want_dk = np.zeros((256, D))
+    want_dv = np.zeros((256, D))
+    for h in range(kv * grp, (kv + 1) * grp):
+        full = oracle.grads(qn[0, h][rows_late], kn[0, kv], vn[0, kv], gn[0, h][rows_late], q_pos=t_late,
+                            causal=True, key_grads=False)
+        part = oracle.grads(qn[0, h][rows_late], kn[0, kv][tok], vn[0, kv][tok], gn[0, h][rows_late], q_pos=t_late,
+                            k_pos=tok, causal=True, lse=full["lse"], delta=full["delta"])
+        want_dk += part["dk"]
+        want_dv += part["dv"]
+    sel_j, sel_c = torch.as_tensor(jj, device="cuda"), torch.as_tensor(cc, device="cuda")
+    gh.grad_close(gh.to_host_f64(dk[sel_j, 0, kv, sel_c]), want_dk, rtol, f"dk kv head {kv}, 256 keys")
+    gh.grad_close(gh.to_host_f64(dv[sel_j, 0, kv, sel_c]), want_dv, rtol, f"dv kv head {kv}, 256 keys")
+    # identities per key/value head
+    dk_h = dk.double().sum(dim=(0, 3))[0]  # [Hkv, D]: over blocks and key rows
+    dv_h = dv.double().sum(dim=(0, 3))[0]
+    g_h = g.double().sum(dim=3)[0, 0].view(Hkv, grp, D).sum(dim=1)  # over the group's heads and the share's rows
+    assert float(torch.max(torch.abs(dk_h))) <= 1e-2 * float(dk.abs().double().sum(dim=(0, 3)).max())
+    assert float(torch.max(torch.abs(dv_h - g_h))) <= 1e-2 * float(torch.max(torch.abs(g_h)) + 1.0)
+
+
 @pytest.mark.parametrize("lay", ["striped", "contiguous"])
 def test_batch2_gqa4_ring_forward_and_backward(lay):
     """Batch 2, 8 query heads on 2 key/value heads, d 64: forward output and lse
