@@ -17,7 +17,8 @@
 // dkdv_kernel -- a wave owns 32 keys, query rows of every query head of the
 // key/value head's group stream through LDS in tiles:
 //     S[q, key]   = Q . K^T          (A: Q tile, row reads;   B: K in registers)
-//     dP[q, key]  = dO . V^T         (A: dO tile, row reads;  B: V in registers)
+//     dP[q, key]  = dO . V^T         (A: dO tile, row reads;  B: V parked in LDS
+//                                     in lane order, one 16-byte read)
 //     dV[key, d] += P^T . dO         (A: P^T from the S accumulators; B: dO tile,
 //                                     transposed reads)
 //     dK[key, d] += dS^T . Q         (A: dS^T; B: Q tile, transposed reads)
@@ -33,13 +34,15 @@
 // dq_kernel runs eight waves in the forward kernel's ping-pong (two groups
 // of one wave per SIMD, half a tile apart); dkdv_kernel runs eight waves
 // (256 keys) that share each query tile, two per SIMD, whose MFMAs and
-// vector work interleave as they fall; a wave raises its priority while it
-// issues its S and dP chains, so that those win the SIMD's issue over the
-// other wave's vector work.
+// vector work interleave as they fall; each wave runs a tile as one
+// software-pipelined MFMA stream (operands read two MFMAs ahead) and raises
+// its priority while it issues its S and dP chains, so that those win the
+// SIMD's issue over the other wave's vector work.
 #include <algorithm>
 #include <climits>
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "mfma_common.h"
 #include "ra_internal.h"
@@ -411,7 +414,9 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
     constexpr int QB = kTile / 32;    // 32-row query blocks per tile
     constexpr int TB = TileCopy<D, kKvWaves>::BYTES;
     constexpr int BUF = 2 * TB + 2 * kTile * 4;                     // Q, dO tiles, lse, delta
-    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF];  // two buffers
+    constexpr int VW = 64 * D;                                       // one wave's V operands
+    // two tile buffers, then each wave's V operands
+    __shared__ __attribute__((aligned(1024))) char smem[2 * BUF + kKvWaves * VW];
 
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -437,6 +442,11 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         kreg[kb] = key_ok ? *reinterpret_cast<const bf16x8*>(kp + key * a.ks[2] + kb * 16 + half * 8) : bf16x8{};
         vreg[kb] = key_ok ? *reinterpret_cast<const bf16x8*>(vp + key * a.vs[2] + kb * 16 + half * 8) : bf16x8{};
     }
+    // V operands parked in LDS in lane order (one 16-byte read per MFMA, no
+    // swizzle: 64 lanes read 1 KiB contiguous), freeing their registers
+    const lds_char* vlane = RA_LDS_PTR(char, smem) + 2 * BUF + wave * VW + lane * 16;
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) *(__attribute__((address_space(3))) bf16x8*)(vlane + kb * 1024) = vreg[kb];
     const float c2 = a.scale * kLog2e;
 
     // rows that see some key of this workgroup / this wave, and rows that see all of this wave's keys
@@ -520,31 +530,47 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         const float* ls = reinterpret_cast<const float*>(smem + (st & 1) * BUF + 2 * TB);
         // edge tiles: the diagonal, the ragged end of the rows, or keys past the block
         const bool edge = rb < wave_row_full || rb + kTile > a.q_len;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            // S = Q K^T, then P; P^T (bf16) feeds dV at once so that the fp32
-            // scores die before dP is formed
-            f32x16 s = f32x16{};
-            __builtin_amdgcn_s_setprio(1);  // the MFMA chain first on this SIMD
-#pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) s = MFMA(rd.rows(qt, qb, kb), kreg[kb], s);
-            __builtin_amdgcn_s_setprio(0);
-            // P; register v holds row rb + 4 half + i of the tile, with the
-            // compile-time i = 32 qb + 8 (v/4) + v%4.  Mask (edge tiles only):
-            // masked scores become -inf, so that their exp2 is exactly 0; a
-            // pair is visible iff i < q_len - rb - 4 half and (causal)
-            // i >= key - mask_offset - rb - 4 half.  Keys past the block need
-            // no mask: each key's dK / dV column is its own and never stored.
+        // One software-pipelined MFMA stream per tile.  For each 32-row block:
+        // S = Q K^T (D/16 MFMAs), P on the vector ALU, dV += P^T dO (D/16),
+        // dP = dO V^T (D/16), dS on the vector ALU, dK += dS^T Q (D/16).  P^T
+        // (bf16) feeds dV at once so that the fp32 scores die before dP is
+        // formed.  Every LDS operand is read kPf steps ahead of its MFMA,
+        // across chain and block boundaries, with a scheduling fence per step
+        // (without the read-ahead each MFMA waited for its operand).
+        constexpr int NS = D / 16, NQ = 4 * NS, NT = QB * NQ, kPf = 2;
+        constexpr int CS = 0, CV = 1, CP = 2, CK = 3;  // chains in stream order: S, dV, dP, dK
+        struct Ops {
+            bf16x8 x, y;
+        };
+        auto load = [&](int n) __attribute__((always_inline)) -> Ops {
+            const int qb = n / NQ, c = (n % NQ) / NS, k = n % NS;
+            Ops o;
+            if (c == CS) {
+                o.x = rd.rows(qt, qb, k);
+            } else if (c == CP) {
+                o.x = rd.rows(gt, qb, k);
+                o.y = ld_row(vlane + k * 1024);
+            } else {
+                o.x = rd.cols(c == CV ? gt : qt, 2 * qb + (k & 1), k >> 1);
+            }
+            return o;
+        };
+        f32x16 s = f32x16{}, dp = f32x16{};
+        bf16x8 p0 = bf16x8{}, p1 = bf16x8{}, d0 = bf16x8{}, d1 = bf16x8{};
+        // P; register v holds row rb + 4 half + i of the tile, with the
+        // compile-time i = 32 qb + 8 (v/4) + v%4.  Mask (edge tiles only):
+        // masked scores become -inf, so that their exp2 is exactly 0; a pair
+        // is visible iff i < q_len - rb - 4 half and (causal)
+        // i >= key - mask_offset - rb - 4 half.  Keys past the block need no
+        // mask: each key's dK / dV column is its own and never stored.
+        auto form_p = [&](int qb) __attribute__((always_inline)) {
             if (edge) {
                 const int r_lim = a.q_len - rb - 4 * half;
                 const int c_lim = a.causal ? key - a.mask_offset - rb - 4 * half : INT_MIN;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 32 * qb + 8 * g + e;
-                        s[4 * g + e] = ((i < r_lim) & (i >= c_lim)) ? s[4 * g + e] : -INFINITY;
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const int i = 32 * qb + 8 * (v / 4) + v % 4;
+                    s[v] = ((i < r_lim) & (i >= c_lim)) ? s[v] : -INFINITY;
                 }
             }
 #pragma unroll
@@ -554,36 +580,53 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
                 for (int e = 0; e < 4; ++e)
                     s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c2, nl4[e]));
             }
-            const bf16x8 p0 = pack_bf16x8(s, 0), p1 = pack_bf16x8(s, 8);
-#pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk) {
-                dv[dblk] = MFMA(p0, rd.cols(gt, 2 * qb, dblk), dv[dblk]);
-                dv[dblk] = MFMA(p1, rd.cols(gt, 2 * qb + 1, dblk), dv[dblk]);
-            }
-            // dP = dO V^T;  dS = P (dP - delta), with P taken back from its bf16 copy
-            f32x16 dp = f32x16{};
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int kb = 0; kb < D / 16; ++kb) dp = MFMA(rd.rows(gt, qb, kb), vreg[kb], dp);
-            __builtin_amdgcn_s_setprio(0);
+            p0 = pack_bf16x8(s, 0);
+            p1 = pack_bf16x8(s, 8);
+        };
+        // dS = P (dP - delta), with P taken back from its bf16 copy
+        auto form_ds = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int rt = 32 * qb + 8 * g + 4 * half;
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + rt);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + 32 * qb + 8 * g + 4 * half);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
-                    const float p = static_cast<float>(v < 8 ? p0[v] : p1[v - 8]);
-                    dp[v] = p * (dp[v] - d4[e]);
+                    const float pv = static_cast<float>(v < 8 ? p0[v] : p1[v - 8]);
+                    dp[v] = pv * (dp[v] - d4[e]);
                 }
             }
-            const bf16x8 d0 = pack_bf16x8(dp, 0), d1 = pack_bf16x8(dp, 8);
+            d0 = pack_bf16x8(dp, 0);
+            d1 = pack_bf16x8(dp, 8);
+        };
+        Ops ops[kPf];
 #pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk) {
-                dk[dblk] = MFMA(d0, rd.cols(qt, 2 * qb, dblk), dk[dblk]);
-                dk[dblk] = MFMA(d1, rd.cols(qt, 2 * qb + 1, dblk), dk[dblk]);
+        for (int n = 0; n < kPf; ++n) ops[n] = load(n);
+        // step n of the stream, n a compile-time constant (a fold over 0 .. NT-1
+        // below, so that no step is left to a runtime loop)
+        auto step = [&]<int n>() __attribute__((always_inline)) {
+            constexpr int qb = n / NQ, c = (n % NQ) / NS, k = n % NS;
+            const Ops op = ops[n % kPf];
+            if constexpr (n + kPf < NT) ops[n % kPf] = load(n + kPf);
+            // a wave raises its priority for its S and dP chains, so that they
+            // win the SIMD's issue over the other wave's vector work
+            if constexpr ((c == CS || c == CP) && k == 0) __builtin_amdgcn_s_setprio(1);
+            if constexpr (c == CS) s = MFMA(op.x, kreg[k], k == 0 ? f32x16{} : s);
+            else if constexpr (c == CV) dv[k >> 1] = MFMA((k & 1) ? p1 : p0, op.x, dv[k >> 1]);
+            else if constexpr (c == CP) dp = MFMA(op.x, op.y, k == 0 ? f32x16{} : dp);
+            else dk[k >> 1] = MFMA((k & 1) ? d1 : d0, op.x, dk[k >> 1]);
+            if constexpr (k == NS - 1 && c == CS) {
+                __builtin_amdgcn_s_setprio(0);
+                form_p(qb);
             }
-        }
+            if constexpr (k == NS - 1 && c == CP) {
+                __builtin_amdgcn_s_setprio(0);
+                form_ds(qb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        [&]<int... N>(std::integer_sequence<int, N...>) __attribute__((always_inline)) {
+            (step.template operator()<N>(), ...);
+        }(std::make_integer_sequence<int, NT>{});
     }
     wait_vmem_all();
 
