@@ -557,6 +557,17 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         };
         f32x16 s = f32x16{}, dp = f32x16{};
         bf16x8 p0 = bf16x8{}, p1 = bf16x8{}, d0 = bf16x8{}, d1 = bf16x8{};
+        // the rows' exp2 offsets (nlp) and delta (dlp), read from LDS when the
+        // S chain (nlp) or the dP chain (dlp) starts, so that P and dS do not
+        // wait for them
+        f32x4 nlp[4], dlp[4];
+        auto load_stats = [&](int qb, bool delta) __attribute__((always_inline)) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                if (delta) dlp[g] = *reinterpret_cast<const f32x4*>(ls + kTile + 32 * qb + 8 * g + 4 * half);
+                else nlp[g] = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 8 * g + 4 * half);
+            }
+        };
         // P; register v holds row rb + 4 half + i of the tile, with the
         // compile-time i = 32 qb + 8 (v/4) + v%4.  Mask (edge tiles only):
         // masked scores become -inf, so that their exp2 is exactly 0; a pair
@@ -575,7 +586,7 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
             }
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 nl4 = *reinterpret_cast<const f32x4*>(ls + 32 * qb + 8 * g + 4 * half);  // exp2 offsets
+                const f32x4 nl4 = nlp[g];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     s[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c2, nl4[e]));
@@ -587,7 +598,7 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
         auto form_ds = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kTile + 32 * qb + 8 * g + 4 * half);
+                const f32x4 d4 = dlp[g];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
@@ -609,7 +620,10 @@ __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(2
             if constexpr (n + kPf < NT) ops[n % kPf] = load(n + kPf);
             // a wave raises its priority for its S and dP chains, so that they
             // win the SIMD's issue over the other wave's vector work
-            if constexpr ((c == CS || c == CP) && k == 0) __builtin_amdgcn_s_setprio(1);
+            if constexpr ((c == CS || c == CP) && k == 0) {
+                __builtin_amdgcn_s_setprio(1);
+                load_stats(qb, c == CP);
+            }
             if constexpr (c == CS) s = MFMA(op.x, kreg[k], k == 0 ? f32x16{} : s);
             else if constexpr (c == CV) dv[k >> 1] = MFMA((k & 1) ? p1 : p0, op.x, dv[k >> 1]);
             else if constexpr (c == CP) dp = MFMA(op.x, op.y, k == 0 ? f32x16{} : dp);
