@@ -712,6 +712,7 @@ hipError_t launch_block_bwd_mfma(const BwdArgs& a, hipStream_t s) {
     if (a.q_len == 0 || a.kv_len == 0) return hipSuccess;
     const int64_t qb = dq_workgroups(a);
     const int64_t kb = dkdv_workgroups(a);
+    if (qb > INT32_MAX || kb > INT32_MAX) return hipErrorInvalidValue;  // one workgroup per tile: 31-bit grids
     if (a.D == 128) {
         hipLaunchKernelGGL(dq_kernel<128>, dim3(static_cast<unsigned>(qb)), dim3(64 * kDqWaves), 0, s, a);
         hipLaunchKernelGGL(dkdv_kernel<128>, dim3(static_cast<unsigned>(kb)), dim3(64 * kKvWaves), 0, s, a);

@@ -313,6 +313,7 @@ hipError_t launch_typed(const BwdArgs& a, hipStream_t s) {
     const int D = a.D;
     const int64_t q_blocks = static_cast<int64_t>((a.q_len + kPerBlock - 1) / kPerBlock) * a.Hq * a.B;
     const int64_t k_blocks = static_cast<int64_t>((a.kv_len + kPerBlock - 1) / kPerBlock) * a.Hkv * a.B;
+    if (q_blocks > INT32_MAX || k_blocks > INT32_MAX) return hipErrorInvalidValue;  // 31-bit grids
     hipError_t e = hipSuccess;
     if (D <= 128) {
         constexpr int C = 32;
@@ -372,6 +373,7 @@ hipError_t launch_bwd_delta(int64_t rows, int32_t D, int dtype, const void* o, c
                             hipStream_t s) {
     if (rows == 0) return hipSuccess;
     const int64_t blocks = (rows + 3) / 4;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;  // four rows a workgroup: 31-bit grids
     if (dtype == 0)
         hipLaunchKernelGGL(delta_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, rows, D,
                            static_cast<const float*>(o), static_cast<const float*>(dout), delta);

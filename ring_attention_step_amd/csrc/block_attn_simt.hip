@@ -181,6 +181,7 @@ template <typename T, int KC>
 hipError_t launch_t(const BlockArgs& a, hipStream_t s) {
     const int n_qt = (a.q_len + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t blocks = static_cast<int64_t>(n_qt) * a.Hq * a.B;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;  // one workgroup per query tile: 31-bit grids
     const size_t lds = sizeof(float) * (2 * KC * (a.D + 1) + kRowsPerBlock * a.D + kWaves * KC);
     hipLaunchKernelGGL((block_simt_kernel<T, KC>), dim3(static_cast<unsigned>(blocks)), dim3(256),
                        lds, s, a);

@@ -185,6 +185,7 @@ hipError_t launch_lse_merge(const MergeArgs& a, hipStream_t s) {
     while (tpr < units && tpr < 64) tpr <<= 1;
     const int64_t rows_per_block = 256 / tpr;
     const int64_t blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;  // grid-per-rows launches: 31-bit grids
     const bool finalize_only = a.o_p == nullptr && a.acc_valid && (a.o_out != nullptr || a.lse_out != nullptr);
     if (vec && finalize_only && (a.D == 128 || a.D == 64)) {
         const int64_t rows_per_block = 4 * RA_FIN_U * (256 / a.D);  // 4 waves x U groups x 64 / (D / 4) rows
